@@ -1,0 +1,211 @@
+/*
+ * moe.h - C ABI of the routed Mixture-of-Experts FFN layer for AMD MI355X (gfx950).
+ *
+ * The layer (as stated on the pages this library follows):
+ *   - hidden size D, E small routed experts of intermediate size I, a router that
+ *     keeps the top_k experts of each token through a softmax, and one always-on
+ *     shared expert ("Systems Engineering Playbook: Qwen 3.5 MoE on Ironwood TPU",
+ *     section "The Architectural Constraints That Break Naive Sharding";
+ *     "Tối ưu hóa mô hình Qwen 3.5-397B MoE trên hạ tầng TPU Ironwood", section
+ *     "3. Sparse Mixture-of-Experts (MoE)");
+ *   - tokens grouped by expert for grouped GEMMs, then unpermuted with a local
+ *     reduction (Playbook, table "Three High-Leverage Optimizations");
+ *   - under expert parallelism one device owns a contiguous slice of the experts,
+ *     receives the routing of all gathered tokens as one packed 32-bit blob of ids
+ *     and weights, and returns partial sums for a reduce-scatter (Playbook, section
+ *     "Fusing Three Collectives Into Two"; "Como o Google otimizou o Qwen 3.5 de
+ *     397B no TPU7x (Ironwood)", section "O problema do sharding e a solução").
+ *
+ * Readings where the pages are silent: routing = softmax over all E fp32 keys,
+ * top_k by (key descending, expert index ascending), weights renormalised over the
+ * kept experts; experts are SwiGLU, out = W_down (silu(W_gate x) * W_up x); the
+ * shared expert has the same form and is added with weight one.
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers, row-major, owned by the caller,
+ *     allocated on the current HIP device.  `dims` and `weights` structs are HOST
+ *     pointers read during the call only.
+ *   - Weights are stored [out][in] (the reduction dimension is contiguous):
+ *       w_router [E][D], w_gate / w_up [n_local][I][D], w_down [n_local][D][I],
+ *       shared gate / up [I_shared][D], shared down [D][I_shared].
+ *   - The packed routing blob is int32 [T][2][top_k]: plane 0 holds expert ids,
+ *     plane 1 the IEEE binary32 bits of the matching weights (token-major, so the
+ *     blobs of several devices concatenate along tokens).
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     is the default stream).  The library never allocates, frees or synchronises
+ *     and keeps no mutable global state; scratch memory is the caller's `ws`
+ *     buffer of at least moe_workspace_bytes(dims) bytes, which must not be shared
+ *     by calls that may run concurrently.
+ *   - Arguments are validated on the host before any launch; on error nothing is
+ *     launched and a negative moe_status is returned.  T = 0 is a successful no-op.
+ *   - Results are deterministic: ids, counts, offsets, permutation are unique
+ *     integers, and every floating-point sum has a fixed order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types. */
+enum moe_dtype {
+  MOE_F32 = 0,  /* IEEE binary32 */
+  MOE_BF16 = 1, /* bfloat16 */
+  MOE_E4M3 = 2  /* OCP FP8 E4M3 (max 448, no infinities), weights only, with fp32 scales */
+};
+
+/* Return codes. */
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL_ARG = -1,    /* a required pointer is NULL */
+  MOE_ERR_BAD_DIMS = -2,    /* T < 0, D/E/I/top_k < 1, top_k > E, expert slice outside [0, E) */
+  MOE_ERR_UNSUPPORTED = -3, /* dtype combination, D or I not a multiple of 64, E > 1024, top_k > 32 */
+  MOE_ERR_WORKSPACE = -4,   /* ws_bytes smaller than moe_workspace_bytes(dims) */
+  MOE_ERR_HIP = -5          /* a kernel launch failed (see moe_last_hip_error) */
+};
+
+/* Problem shape. */
+typedef struct moe_dims {
+  int32_t T;            /* tokens (rows of x) */
+  int32_t D;            /* hidden size */
+  int32_t E;            /* routed experts of the whole layer */
+  int32_t top_k;        /* experts kept per token */
+  int32_t I;            /* intermediate size of a routed expert */
+  int32_t I_shared;     /* intermediate size of the shared expert; 0 = no shared expert */
+  int32_t expert_begin; /* first local expert id (0 for the whole layer) */
+  int32_t n_local;      /* local experts: ids expert_begin .. expert_begin + n_local - 1 */
+  int32_t renormalize;  /* 1: kept weights sum to 1; 0: kept softmax entries as they are */
+  int32_t act_dtype;    /* x, router weight, shared weights: MOE_F32 or MOE_BF16 */
+  int32_t w_dtype;      /* routed expert weights: MOE_F32 (with act F32), MOE_BF16 or MOE_E4M3 (with act BF16) */
+  int32_t out_dtype;    /* y and expert outputs: MOE_F32 or MOE_BF16 */
+} moe_dims;
+
+/* Weights of the layer (device pointers). */
+typedef struct moe_weights {
+  const void* w_router;  /* [E][D] act_dtype; may be NULL when routing is given */
+  const void* w_gate;    /* [n_local][I][D] w_dtype */
+  const void* w_up;      /* [n_local][I][D] w_dtype */
+  const void* w_down;    /* [n_local][D][I] w_dtype */
+  const float* s_gate;   /* [n_local][I] per-output-channel scales (E4M3 only, else NULL) */
+  const float* s_up;     /* [n_local][I] */
+  const float* s_down;   /* [n_local][D] */
+  const void* sh_gate;   /* [I_shared][D] act_dtype (NULL if I_shared == 0) */
+  const void* sh_up;     /* [I_shared][D] */
+  const void* sh_down;   /* [D][I_shared] */
+} moe_weights;
+
+/*
+ * Scratch bytes needed by any entry point for these dims (upper bound over all
+ * routings).  Returns 0 if the dims are invalid.
+ */
+size_t moe_workspace_bytes(const moe_dims* dims);
+
+/*
+ * Router: top-k selection and weights, written as the packed blob.
+ *   logits[t][e] = sum_d x[t][d] * w_router[e][d]   (fp32 accumulation)
+ *   key = fp32(logit + logit_bias[e]); keep the top_k keys (larger first, equal
+ *   key -> lower expert id); w_j = exp(key_j - key_0) / sum_i exp(key_i - key_0)
+ *   over the kept keys (renormalize = 1), or over all E (renormalize = 0).
+ * Source: the router of "3. Sparse Mixture-of-Experts (MoE)" (Tối ưu hóa ... TPU
+ * Ironwood); the packed blob of Playbook "Fusing Three Collectives Into Two".
+ *
+ *   x          [T][D] act_dtype, or NULL
+ *   w_router   [E][D] act_dtype, or NULL
+ *   logits     [T][E] fp32: OUTPUT when x and w_router are given; INPUT when both
+ *              are NULL (route from caller-supplied logits).
+ *   logit_bias [E] fp32 or NULL (an additive popularity bias; -inf never chosen).
+ *              Each token needs at least top_k finite keys; NaN is not supported.
+ *   packed     [T][2][top_k] int32 output.
+ */
+int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* logits,
+              const float* logit_bias, int32_t* packed, void* stream);
+
+/*
+ * Permutation: group the (token, slot) pairs whose expert is local by expert
+ * (experts ascending, (t, j) ascending inside an expert).  Ids outside the local
+ * slice (other devices' experts, or any value outside [0, E)) are skipped.
+ *
+ *   packed     [T][2][top_k] int32 input
+ *   counts     [n_local] int32 out: rows of each local expert
+ *   offsets    [n_local + 1] int32 out: exclusive prefix sum; offsets[n_local] = N_a
+ *   perm_token [T * top_k] int32 out: first N_a entries = source token of each row
+ *   inv_pos    [T][top_k] int32 out: grouped row of (t, j), or -1 if not local
+ *   x          [T][D] act_dtype, optional (NULL: index-only)
+ *   x_perm     [T * top_k][D] optional gather target: act_dtype, or E4M3 codes when
+ *              w_dtype is E4M3 (x is then quantised per token first)
+ *   x_perm_scale [T * top_k] fp32, E4M3 only: per-row dequantisation scale
+ */
+int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, int32_t* offsets,
+                int32_t* perm_token, int32_t* inv_pos, const void* x, void* x_perm,
+                float* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped SwiGLU experts on ragged groups:
+ *   for each local expert e and each row r in [offsets[e], offsets[e+1]):
+ *     h = silu(W_gate[e] a_r) * (W_up[e] a_r);  out_rows[r] = W_down[e] h
+ * Source: the "Grouped GEMMs" block of the Playbook's introduction and table.
+ *
+ *   a_rows     if perm_token is NULL: grouped rows [N_a][D]; else x [T][D] and row r
+ *              reads x[perm_token[r]].  act_dtype, or E4M3 codes when w_dtype is E4M3.
+ *   a_scale    E4M3 only: fp32 scale per row of a_rows ([N_a], or [T] with perm_token)
+ *   perm_token [N_a] int32 or NULL
+ *   offsets    [n_local + 1] int32 (device)
+ *   weights    local slice, see moe_weights; scales only for E4M3
+ *   out_rows   [T * top_k][D] out_dtype: unweighted expert outputs of the grouped rows
+ * The shared expert is not part of this call (call it with n_local = 1,
+ * offsets = {0, T}, perm_token = NULL and I = I_shared to evaluate it alone).
+ */
+int moe_grouped_ffn(const moe_dims* dims, const void* a_rows, const float* a_scale,
+                    const int32_t* perm_token, const int32_t* offsets, const void* w_gate,
+                    const void* w_up, const void* w_down, const float* s_gate, const float* s_up,
+                    const float* s_down, void* out_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Unpermute and reduce ("unpermutation + local reduction", Playbook table
+ * "Three High-Leverage Optimizations"):
+ *   y[t] = sum_{j : inv_pos[t][j] >= 0} w[t][j] * out_rows[inv_pos[t][j]]  (+ shared_out[t])
+ * summed in fp32 in slot order, the shared row added last, rounded once to out_dtype.
+ *
+ *   out_rows   [N_a][D] out_dtype
+ *   packed     [T][2][top_k] int32 (weights are read from plane 1)
+ *   inv_pos    [T][top_k] int32
+ *   shared_out [T][D] out_dtype or NULL
+ *   y          [T][D] out_dtype
+ */
+int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int32_t* packed,
+                          const int32_t* inv_pos, const void* shared_out, void* y, void* stream);
+
+/*
+ * The whole layer: route -> permute -> grouped experts (+ shared expert) -> combine.
+ *
+ *   x          [T][D] act_dtype
+ *   packed_in  [T][2][top_k] int32 or NULL.  Non-NULL: the routing is given (one
+ *              device's expert-parallel share) and the router is skipped.
+ *   logit_bias [E] fp32 or NULL (router only)
+ *   y          [T][D] out_dtype.  With a local slice: the slice's partial sums
+ *              (zero rows for tokens without a local expert).
+ *   logits_out [T][E] fp32 or NULL: copy of the router logits
+ *   packed_out [T][2][top_k] int32 or NULL: copy of the routing blob
+ */
+int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const void* x,
+                      const int32_t* packed_in, const float* logit_bias, void* y, float* logits_out,
+                      int32_t* packed_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable text of a moe_status code (static storage). */
+const char* moe_status_string(int status);
+
+/* hipError_t of the last failed launch on the calling host thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* ABI version of this header: 1. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,174 @@
+"""Routed Mixture-of-Experts FFN layer for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libmoe_hip.so`` (C ABI in ``include/moe.h``).  The
+functions below carry the C names and only marshal arguments: torch tensors
+become device pointers, the current torch stream becomes the HIP stream.
+Every step of the layer runs in the library's HIP kernels; there is no
+fallback.  Loading fails loudly when the library has not been built
+(``python -m sparse_moe_ffn_route_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
+
+# enum moe_dtype
+F32, BF16, E4M3 = 0, 1, 2
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
+_TORCH_OF = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.float8_e4m3fn}
+
+# enum moe_status
+OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+# Symbols exported by the library (the entry points of include/moe.h).
+EXPORTS = (
+    "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine",
+    "moe_layer_forward", "moe_status_string", "moe_last_hip_error", "moe_abi_version",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status}")
+        self.status = status
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "D", "E", "top_k", "I", "I_shared", "expert_begin", "n_local", "renormalize",
+        "act_dtype", "w_dtype", "out_dtype")]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down")]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libmoe_hip.so`` (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_ffn_route_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dp, wp = ctypes.POINTER(moe_dims), ctypes.POINTER(moe_weights)
+    lib.moe_workspace_bytes.argtypes = [dp]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_route.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route.restype = i32
+    lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_permute.restype = i32
+    lib.moe_grouped_ffn.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_grouped_ffn.restype = i32
+    lib.moe_unpermute_combine.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.moe_unpermute_combine.restype = i32
+    lib.moe_layer_forward.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_layer_forward.restype = i32
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_hip_error.argtypes = []
+    lib.moe_last_hip_error.restype = i32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def make_dims(T, D, E, top_k, I, I_shared=0, expert_begin=0, n_local=None, renormalize=True,
+              act="bf16", w="bf16", out="bf16") -> moe_dims:
+    return moe_dims(T, D, E, top_k, I, I_shared, expert_begin, E if n_local is None else n_local,
+                    1 if renormalize else 0, _DTYPE_CODE[act], _DTYPE_CODE[w], _DTYPE_CODE[out])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or None")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        lib = library()
+        msg = lib.moe_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {lib.moe_last_hip_error()})"
+        raise MoeError(status, f"{what}: {msg}")
+
+
+def moe_workspace_bytes(dims: moe_dims) -> int:
+    return int(library().moe_workspace_bytes(ctypes.byref(dims)))
+
+
+def workspace(dims: moe_dims, device="cuda") -> torch.Tensor:
+    """A caller-owned scratch buffer of moe_workspace_bytes(dims) bytes."""
+    n = moe_workspace_bytes(dims)
+    if n == 0:
+        raise MoeError(ERR_BAD_DIMS, "moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(dims, x, w_router, logits, logit_bias, packed, stream=None):
+    _check(library().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(logit_bias),
+                               _ptr(packed), _stream(stream)), "moe_route")
+
+
+def moe_permute(dims, packed, counts, offsets, perm_token, inv_pos, x=None, x_perm=None, x_perm_scale=None,
+                ws=None, stream=None):
+    _check(library().moe_permute(ctypes.byref(dims), _ptr(packed), _ptr(counts), _ptr(offsets), _ptr(perm_token),
+                                 _ptr(inv_pos), _ptr(x), _ptr(x_perm), _ptr(x_perm_scale), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_grouped_ffn(dims, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                    out_rows, ws, stream=None):
+    _check(library().moe_grouped_ffn(ctypes.byref(dims), _ptr(a_rows), _ptr(a_scale), _ptr(perm_token),
+                                     _ptr(offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate),
+                                     _ptr(s_up), _ptr(s_down), _ptr(out_rows), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_unpermute_combine(dims, out_rows, packed, inv_pos, shared_out, y, stream=None):
+    _check(library().moe_unpermute_combine(ctypes.byref(dims), _ptr(out_rows), _ptr(packed), _ptr(inv_pos),
+                                           _ptr(shared_out), _ptr(y), _stream(stream)), "moe_unpermute_combine")
+
+
+def make_weights(w_router=None, w_gate=None, w_up=None, w_down=None, s_gate=None, s_up=None, s_down=None,
+                 sh_gate=None, sh_up=None, sh_down=None) -> moe_weights:
+    """moe_weights from tensors; the tensors must stay alive while the struct is used."""
+    return moe_weights(*[_ptr(t) for t in (w_router, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                                           sh_gate, sh_up, sh_down)])
+
+
+def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, logits_out=None, packed_out=None,
+                      ws=None, stream=None):
+    _check(library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _ptr(packed_in),
+                                       _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_forward")
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return _TORCH_OF[code]

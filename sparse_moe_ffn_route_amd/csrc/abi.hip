@@ -1,0 +1,351 @@
+// C ABI of the MoE layer: argument validation, workspace layout, launch sequences.
+// Every check happens on the host before the first launch; the library never
+// allocates, frees or synchronises.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+int act_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
+int out_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
+int w_el(const moe_dims& d) { return d.w_dtype; }
+int h_el(const moe_dims& d) { return d.act_dtype == MOE_F32 ? EL_F32 : EL_BF16; }
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_ERR_NULL_ARG;
+  if (d->T < 0 || d->D < 1 || d->E < 1 || d->I < 1 || d->top_k < 1 || d->top_k > d->E) return MOE_ERR_BAD_DIMS;
+  if (d->I_shared < 0 || d->expert_begin < 0 || d->n_local < 1 ||
+      static_cast<int64_t>(d->expert_begin) + d->n_local > d->E)
+    return MOE_ERR_BAD_DIMS;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_BAD_DIMS;
+  if (d->top_k > 32 || d->E > 1024 || d->n_local > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
+  if (d->D % 64 || d->I % 64 || d->I_shared % 64) return MOE_ERR_UNSUPPORTED;
+  const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32 && d->out_dtype == MOE_F32;
+  const bool bf16 = d->act_dtype == MOE_BF16 && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_E4M3) &&
+                    (d->out_dtype == MOE_BF16 || d->out_dtype == MOE_F32);
+  if (!f32 && !bf16) return MOE_ERR_UNSUPPORTED;
+  // every row index and byte offset below fits the kernels' integer types
+  const int64_t tk = static_cast<int64_t>(d->T) * d->top_k;
+  if (tk > (1ll << 30) || static_cast<int64_t>(d->T) * d->E > (1ll << 31) - 1) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t logits, packed, hist, base, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
+  size_t xq, sx, h, h_sh, hq, sh, out_rows, sh_out, total;
+};
+
+Layout layout(const moe_dims& d) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t T = d.T, tk = static_cast<size_t>(d.T) * d.top_k, nl = d.n_local;
+  const size_t U = perm_units(d.T, d.top_k);
+  const bool fp8 = d.w_dtype == MOE_E4M3;
+  const size_t hs = act_size(d.act_dtype), os = out_size(d.out_dtype);
+  L.logits = take(T * d.E * 4);
+  L.packed = take(tk * 2 * 4);
+  L.hist = take(nl * U * 4);
+  L.base = take(nl * U * 4);
+  L.counts = take(nl * 4);
+  L.offsets = take((nl + 1) * 4);
+  L.tp_a = take((nl + 1) * 4);
+  L.tp_b = take((nl + 1) * 4);
+  L.perm_token = take(tk * 4);
+  L.inv_pos = take(tk * 4);
+  L.xq = take(fp8 ? T * d.D : 0);
+  L.sx = take(fp8 ? T * 4 : 0);
+  L.h = take(tk * d.I * hs);
+  L.h_sh = take(T * d.I_shared * hs);
+  L.hq = take(fp8 ? tk * d.I : 0);
+  L.sh = take(fp8 ? tk * 4 : 0);
+  L.out_rows = take(tk * d.D * os);
+  L.sh_out = take(d.I_shared ? T * d.D * os : 0);
+  L.total = off;
+  return L;
+}
+
+template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<uint8_t*>(ws) + off); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MOE_ERR_HIP;
+}
+
+#define MOE_TRY(expr)                        \
+  do {                                       \
+    const int _s = hip_status(expr);         \
+    if (_s != MOE_OK) return _s;             \
+  } while (0)
+
+// Tiles per M-row fragment count: average routed rows per expert decides.
+int choose_mf(const moe_dims& d) {
+  const double avg = static_cast<double>(d.T) * d.top_k / d.E;
+  return avg <= 16.0 ? 1 : 2;
+}
+
+int routed_tile_bound(int rows_total, int n_groups, int bm, int n, int bn) {
+  const int64_t mt = (static_cast<int64_t>(rows_total) + static_cast<int64_t>(n_groups) * (bm - 1)) / bm;
+  return static_cast<int>(mt * ((n + bn - 1) / bn));
+}
+
+constexpr int kBnSwiglu = 64, kBnPlain = 128;
+
+GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, int lda, const int32_t* offsets,
+                    const int32_t* tile_prefix, int n_groups, int rows, const void* w0, const void* w1,
+                    const float* s0, const float* s1, long long w_stride, void* out, int ldo, int N, int K) {
+  GemmProblem p;
+  p.a = a; p.perm = perm; p.a_scale = a_scale; p.lda = lda;
+  p.offsets = offsets; p.tile_prefix = tile_prefix; p.n_groups = n_groups; p.rows = rows;
+  p.w0 = w0; p.w1 = w1; p.s0 = s0; p.s1 = s1; p.w_stride = w_stride;
+  p.out = out; p.ldo = ldo; p.N = N; p.K = K;
+  return p;
+}
+
+int router_logits(const moe_dims& d, const void* x, const void* w_router, float* logits, hipStream_t s) {
+  const GemmProblem p = problem(x, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, w_router, nullptr, nullptr,
+                                nullptr, 0, logits, d.E, d.E, d.D);
+  const int mf = 2;
+  const int tiles = ((d.T + 16 * mf - 1) / (16 * mf)) * ((d.E + kBnPlain - 1) / kBnPlain);
+  return hip_status(launch_gemm(d.act_dtype, EL_F32, false, mf, p, nullptr, tiles, s));
+}
+
+// gate/up -> h (+ quantise) -> down for the routed groups, with an optional shared
+// expert evaluated as one more problem of the same launches.
+int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_rows, const float* a_scale,
+                    const int32_t* perm, const int32_t* offsets, const void* w_gate, const void* w_up,
+                    const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
+                    void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
+                    const void* sh_down, void* sh_out, hipStream_t s) {
+  const int mf = choose_mf(d);
+  const int bm = gemm_bm(mf);
+  const int tk = d.T * d.top_k;
+  const bool fp8 = d.w_dtype == MOE_E4M3;
+  int32_t* tp_a = at<int32_t>(ws, L.tp_a);
+  int32_t* tp_b = at<int32_t>(ws, L.tp_b);
+  void* h = at<void>(ws, L.h);
+  void* h_sh = at<void>(ws, L.h_sh);
+  const int32_t* n_rows_dev = offsets + d.n_local;
+  const int hel = h_el(d);
+  const bool shared = d.I_shared > 0 && sh_gate;
+
+  MOE_TRY(launch_tile_prefix(offsets, d.n_local, bm, bm, tp_a, tp_b, s));
+
+  // gate/up with the fused SwiGLU epilogue
+  const GemmProblem g0 = problem(a_rows, perm, a_scale, d.D, offsets, tp_a, d.n_local, 0, w_gate, w_up, s_gate, s_up,
+                                 static_cast<long long>(d.I) * d.D, h, d.I, d.I, d.D);
+  const int tiles_gu = routed_tile_bound(tk, d.n_local, bm, d.I, kBnSwiglu);
+  GemmProblem gs{};
+  if (shared)
+    gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr, nullptr, 0, h_sh,
+                 d.I_shared, d.I_shared, d.D);
+  if (shared && !fp8) {
+    MOE_TRY(launch_gemm(w_el(d), hel, true, mf, g0, &gs, tiles_gu, s));
+  } else {
+    MOE_TRY(launch_gemm(w_el(d), hel, true, mf, g0, nullptr, tiles_gu, s));
+    if (shared)
+      MOE_TRY(launch_gemm(d.act_dtype, hel, true, mf, gs, nullptr,
+                          ((d.T + bm - 1) / bm) * ((d.I_shared + kBnSwiglu - 1) / kBnSwiglu), s));
+  }
+
+  // down projection of every grouped row
+  const void* h_in = h;
+  const float* h_scale = nullptr;
+  if (fp8) {
+    void* hq = at<void>(ws, L.hq);
+    float* sh = at<float>(ws, L.sh);
+    MOE_TRY(launch_quant_rows(EL_BF16, h, tk, n_rows_dev, d.I, hq, sh, s));
+    h_in = hq;
+    h_scale = sh;
+  }
+  const GemmProblem d0 = problem(h_in, nullptr, h_scale, d.I, offsets, tp_b, d.n_local, 0, w_down, nullptr, s_down,
+                                 nullptr, static_cast<long long>(d.D) * d.I, out_rows, d.D, d.D, d.I);
+  const int tiles_dn = routed_tile_bound(tk, d.n_local, bm, d.D, kBnPlain);
+  GemmProblem ds{};
+  if (shared)
+    ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr, nullptr, nullptr, 0,
+                 sh_out, d.D, d.D, d.I_shared);
+  const int oel = d.out_dtype;
+  if (shared && !fp8) {
+    MOE_TRY(launch_gemm(w_el(d), oel, false, mf, d0, &ds, tiles_dn, s));
+  } else {
+    MOE_TRY(launch_gemm(w_el(d), oel, false, mf, d0, nullptr, tiles_dn, s));
+    if (shared)
+      MOE_TRY(launch_gemm(d.act_dtype, oel, false, mf, ds, nullptr,
+                          ((d.T + bm - 1) / bm) * ((d.D + kBnPlain - 1) / kBnPlain), s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_dims* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return layout(*dims).total;
+}
+
+int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* logits, const float* logit_bias,
+              int32_t* packed, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!logits || !packed) return MOE_ERR_NULL_ARG;
+  if ((x == nullptr) != (w_router == nullptr)) return MOE_ERR_NULL_ARG;
+  if (d.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (x) {
+    st = router_logits(d, x, w_router, logits, s);
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_route(logits, logit_bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
+}
+
+int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                int32_t* inv_pos, const void* x, void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!packed || !counts || !offsets || !perm_token || !inv_pos || !ws) return MOE_ERR_NULL_ARG;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_NULL_ARG;
+  const bool fp8 = d.w_dtype == MOE_E4M3;
+  if (x && fp8 && !x_perm_scale) return MOE_ERR_NULL_ARG;
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.T == 0) return MOE_OK;
+  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
+                         at<int32_t>(ws, L.base), counts, offsets, perm_token, inv_pos, s));
+  if (x) {
+    const int tk = d.T * d.top_k;
+    if (fp8) {
+      MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s));
+      MOE_TRY(launch_gather_rows(at<void>(ws, L.xq), at<float>(ws, L.sx), perm_token, offsets + d.n_local, tk, d.D,
+                                 x_perm, x_perm_scale, s));
+    } else {
+      MOE_TRY(launch_gather_rows(x, nullptr, perm_token, offsets + d.n_local, tk, d.D * act_size(d.act_dtype), x_perm,
+                                 nullptr, s));
+    }
+  }
+  return MOE_OK;
+}
+
+int moe_grouped_ffn(const moe_dims* dims, const void* a_rows, const float* a_scale, const int32_t* perm_token,
+                    const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
+                    const float* s_gate, const float* s_up, const float* s_down, void* out_rows, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!a_rows || !offsets || !w_gate || !w_up || !w_down || !out_rows || !ws) return MOE_ERR_NULL_ARG;
+  const bool fp8 = d.w_dtype == MOE_E4M3;
+  if (fp8 && (!a_scale || !s_gate || !s_up || !s_down)) return MOE_ERR_NULL_ARG;
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d.T == 0) return MOE_OK;
+  return experts_forward(d, ws, L, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,
+                          const void* shared_out, void* y, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!out_rows || !packed || !inv_pos || !y) return MOE_ERR_NULL_ARG;
+  if (d.T == 0) return MOE_OK;
+  return hip_status(launch_combine(d.out_dtype, out_rows, packed, inv_pos, shared_out, d.T, d.D, d.top_k, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x, const int32_t* packed_in,
+                      const float* logit_bias, void* y, float* logits_out, int32_t* packed_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!w || !x || !y || !ws) return MOE_ERR_NULL_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL_ARG;
+  if (!packed_in && !w->w_router) return MOE_ERR_NULL_ARG;
+  const bool fp8 = d.w_dtype == MOE_E4M3;
+  if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL_ARG;
+  if (d.I_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_NULL_ARG;
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // 1. routing
+  const int32_t* packed = packed_in;
+  if (!packed_in) {
+    float* logits = logits_out ? logits_out : at<float>(ws, L.logits);
+    int32_t* pk = packed_out ? packed_out : at<int32_t>(ws, L.packed);
+    st = router_logits(d, x, w->w_router, logits, s);
+    if (st != MOE_OK) return st;
+    MOE_TRY(launch_route(logits, logit_bias, d.T, d.E, d.top_k, d.renormalize, pk, s));
+    packed = pk;
+  } else if (packed_out) {
+    MOE_TRY(hipMemcpyAsync(packed_out, packed_in, static_cast<size_t>(d.T) * 2 * d.top_k * 4,
+                           hipMemcpyDeviceToDevice, s));
+  }
+
+  // 2. grouping by expert
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm_token);
+  int32_t* inv = at<int32_t>(ws, L.inv_pos);
+  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
+                         at<int32_t>(ws, L.base), counts, offsets, perm, inv, s));
+
+  // 3. experts (+ shared)
+  const void* a_rows = x;
+  const float* a_scale = nullptr;
+  if (fp8) {
+    MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s));
+    a_rows = at<void>(ws, L.xq);
+    a_scale = at<float>(ws, L.sx);
+  }
+  void* out_rows = at<void>(ws, L.out_rows);
+  void* sh_out = d.I_shared ? at<void>(ws, L.sh_out) : nullptr;
+  st = experts_forward(d, ws, L, a_rows, a_scale, perm, offsets, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up,
+                       w->s_down, out_rows, x, d.I_shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, sh_out, s);
+  if (st != MOE_OK) return st;
+
+  // 4. unpermute + weighted combine (+ shared)
+  return hip_status(launch_combine(d.out_dtype, out_rows, packed, inv, sh_out, d.T, d.D, d.top_k, y, s));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case MOE_ERR_BAD_DIMS: return "invalid dimensions";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dimensions or dtype combination";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_abi_version(void) { return 1; }
+
+}  // extern "C"

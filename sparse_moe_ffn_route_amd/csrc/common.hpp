@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Element types of GEMM operands and outputs (same values as enum moe_dtype).
+enum : int { EL_F32 = 0, EL_BF16 = 1, EL_E4M3 = 2 };
+
+template <int EL> struct ElSize;
+template <> struct ElSize<EL_F32> { static constexpr int v = 4; };
+template <> struct ElSize<EL_BF16> { static constexpr int v = 2; };
+template <> struct ElSize<EL_E4M3> { static constexpr int v = 1; };
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> bfloat16 bits, round to nearest even (finite inputs; infinities stay infinite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> two OCP E4M3 codes in the low 16 bits (hardware convert, nearest even).
+// Callers clamp to +-448 first, so the convert never sees an out-of-range value.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// One 16-byte K-chunk per lane through the 16x16 MFMA family.
+//
+// A wave holds a 16-row A tile and a 16-column B tile, each lane carrying 16
+// contiguous bytes of its row (A) / column (B) at K-offset (lane / 16) * 16 bytes.
+// The four lane groups therefore cover 64 contiguous bytes of K; the element
+// order inside the MFMA is the same for A and B, so the dot products are the
+// plain K-sums.  The accumulator layout is the 16x16 MFMA one: lane l holds
+// C[(l / 16) * 4 + r][l % 16], r = 0..3 (row of A, column of B).
+// ---------------------------------------------------------------------------
+
+template <int EL> __device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x4 c);
+
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_BF16>(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_F32>(const uint4& a, const uint4& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_E4M3>(const uint4& a, const uint4& b, f32x4 c) {
+  long a0 = static_cast<long>((static_cast<uint64_t>(a.y) << 32) | a.x);
+  long a1 = static_cast<long>((static_cast<uint64_t>(a.w) << 32) | a.z);
+  long b0 = static_cast<long>((static_cast<uint64_t>(b.y) << 32) | b.x);
+  long b1 = static_cast<long>((static_cast<uint64_t>(b.w) << 32) | b.z);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Map a linear block index onto a contiguous range of logical tiles per XCD.
+// Blocks are dispatched round-robin over the 8 XCDs of an MI355X, so block b runs on
+// XCD b % 8; giving each XCD one contiguous range keeps tiles that share operands
+// (the same expert's weights, the same token rows) in one L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int q = total / 8, r = total % 8;
+  const int xcd = b % 8, local = b / 8;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+}  // namespace moe

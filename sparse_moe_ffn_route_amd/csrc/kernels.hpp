@@ -1,0 +1,68 @@
+// Host-side launch interface of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxLocalExperts = 1024;  // LDS histogram rows of the permutation
+constexpr int kPermUnit = 1024;         // (token, slot) pairs per permutation wave
+
+inline int perm_units(int T, int k) { return (T * k + kPermUnit - 1) / kPermUnit; }
+
+// One GEMM problem of the grouped expert kernels.  Rows of group g are
+// [offsets[g], offsets[g+1]) (or one group of `rows` rows when offsets is NULL);
+// row r of a group reads A row perm[r] (or r when perm is NULL).  Weights are
+// [n_groups][N][K] ([out][in]); out is [rows][ldo] at the grouped row index.
+struct GemmProblem {
+  const void* a;
+  const int32_t* perm;
+  const float* a_scale;        // E4M3: per A-source-row scale
+  int lda;                     // elements
+  const int32_t* offsets;      // device, [n_groups + 1], or NULL
+  const int32_t* tile_prefix;  // device, [n_groups + 1] M-tile prefix for this kernel's BM
+  int n_groups;
+  int rows;                    // rows of the single group when offsets is NULL
+  const void* w0;              // gate (SwiGLU) or the only weight
+  const void* w1;              // up (SwiGLU)
+  const float* s0;             // E4M3 per-output-channel scales [n_groups][N]
+  const float* s1;
+  long long w_stride;          // elements between consecutive groups' weights
+  void* out;
+  int ldo;                     // elements
+  int N, K;
+};
+
+// Which tile height a launch uses.
+int gemm_bm(int mf);
+
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k, int renormalize,
+                        int32_t* packed, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
+                          int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
+                          hipStream_t stream);
+
+hipError_t launch_gather_rows(const void* src, const float* src_scale, const int32_t* perm_token,
+                              const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,
+                              hipStream_t stream);
+
+hipError_t launch_quant_rows(int in_el, const void* src, int rows, const int32_t* n_rows_dev, int cols, void* dst,
+                             float* scale, hipStream_t stream);
+
+hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int bm1, int32_t* prefix0,
+                              int32_t* prefix1, hipStream_t stream);
+
+// Grouped GEMM over up to two problems in one launch (p1 may be NULL).
+//   swiglu: out = silu(A W0^T) * (A W1^T);  else out = A W0^T.
+//   el: operand type (EL_F32 / EL_BF16 / EL_E4M3); out_el: EL_F32 / EL_BF16.
+//   mf: 16-row fragments per tile (1 or 2).
+//   max_tiles0: host upper bound of p0's tiles (its grid share).
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int mf, const GemmProblem& p0, const GemmProblem* p1,
+                       int max_tiles0, hipStream_t stream);
+
+hipError_t launch_combine(int out_el, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,
+                          const void* shared_out, int T, int D, int k, void* y, hipStream_t stream);
+
+}  // namespace moe

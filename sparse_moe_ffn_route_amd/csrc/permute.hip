@@ -1,0 +1,288 @@
+// Grouping (token, slot) pairs by expert, its inverse map, row gathers and the
+// per-row E4M3 quantiser.
+//
+// Source: the grouped GEMMs and the "unpermutation + local reduction" of
+// "Systems Engineering Playbook: Qwen 3.5 MoE on Ironwood TPU" (table "Three
+// High-Leverage Optimizations") need the rows of each expert contiguous; under
+// expert parallelism only the device's own expert slice is grouped (section
+// "Fusing Three Collectives Into Two").
+//
+// Deterministic without atomics deciding positions:
+//   1. histogram: the token-major list of T*k pairs is cut into units of 1024 pairs,
+//      one wave per unit, counted in a per-wave LDS histogram -> hist[e][unit];
+//   2. scan: one workgroup scans hist in expert-major order -> base[e][unit],
+//      offsets, counts;
+//   3. scatter: each wave re-walks its unit 64 pairs at a time; lanes holding the
+//      same expert find each other with one ballot per bit of the expert id, rank
+//      themselves by lane order, and the lowest lane advances that expert's running
+//      count.  Row = base[e][unit] + running + rank, i.e. (t, j) order within each
+//      expert.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ int pair_expert(const int32_t* packed, int i, int k) {
+  const int t = i / k, j = i - t * k;
+  return packed[static_cast<size_t>(t) * 2 * k + j];
+}
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
+                                                        int e_begin, int n_local, int n_units,
+                                                        int32_t* __restrict__ hist) {
+  __shared__ int32_t h[kWavesPerBlock][kMaxLocalExperts];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int u = blockIdx.x * kWavesPerBlock + w;
+  if (u >= n_units) return;  // whole wave leaves together; waves use disjoint LDS rows
+  for (int e = lane; e < n_local; e += kWave) h[w][e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  const int end = min(n_pairs, (u + 1) * kPermUnit);
+  for (int i = u * kPermUnit + lane; i < end; i += kWave) {
+    const int e = pair_expert(packed, i, k) - e_begin;
+    if (e >= 0 && e < n_local) atomicAdd(&h[w][e], 1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < n_local; e += kWave) hist[static_cast<size_t>(e) * n_units + u] = h[w][e];
+}
+
+// One workgroup of 1024 threads: exclusive scan of hist (expert-major) into base.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int n_local,
+                                                         int n_units, int32_t* __restrict__ base,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  const int n = n_local * n_units;
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += hist[i];
+  part[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;  // exclusive prefix of this thread's chunk
+  for (int i = lo; i < hi; ++i) {
+    const int c = hist[i];
+    base[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  const int total = part[1023];
+  for (int e = tid; e < n_local; e += 1024) {
+    const int b0 = base[static_cast<size_t>(e) * n_units];
+    const int b1 = (e + 1 < n_local) ? base[static_cast<size_t>(e + 1) * n_units] : total;
+    offsets[e] = b0;
+    counts[e] = b1 - b0;
+  }
+  if (tid == 0) offsets[n_local] = total;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ packed, int n_pairs,
+                                                           int k, int e_begin, int n_local, int n_bits,
+                                                           int n_units, const int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ perm_token,
+                                                           int32_t* __restrict__ inv_pos) {
+  __shared__ int32_t run[kWavesPerBlock][kMaxLocalExperts];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int u = blockIdx.x * kWavesPerBlock + w;
+  if (u >= n_units) return;
+  for (int e = lane; e < n_local; e += kWave) run[w][e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int end = min(n_pairs, (u + 1) * kPermUnit);
+  for (int i0 = u * kPermUnit; i0 < end; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool valid = i < end;
+    const int e = valid ? pair_expert(packed, i, k) - e_begin : -1;
+    const bool local = valid && e >= 0 && e < n_local;
+    uint64_t same = __ballot(local);
+    for (int b = 0; b < n_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(local && bit);
+      same &= bit ? m : ~m;
+    }
+    int pos = -1;
+    if (local) {
+      const int rank = __popcll(same & below);
+      pos = base[static_cast<size_t>(e) * n_units + u] + run[w][e] + rank;
+      perm_token[pos] = i / k;
+    }
+    __builtin_amdgcn_wave_barrier();  // every lane has read run[] before the leaders advance it
+    if (local && __popcll(same & below) == 0) run[w][e] += __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) inv_pos[i] = pos;
+  }
+}
+
+// Row gather: dst[r] = src[perm_token[r]] for r < offsets[n_local]; bytes per row
+// must be a multiple of 16.  One 256-thread block per row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src,
+                                                          const float* __restrict__ src_scale,
+                                                          const int32_t* __restrict__ perm_token,
+                                                          const int32_t* __restrict__ n_rows_dev,
+                                                          int row_bytes, uint8_t* __restrict__ dst,
+                                                          float* __restrict__ dst_scale) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows_dev) return;
+  const int t = perm_token[r];
+  const uint4* s = reinterpret_cast<const uint4*>(src + static_cast<size_t>(t) * row_bytes);
+  uint4* d = reinterpret_cast<uint4*>(dst + static_cast<size_t>(r) * row_bytes);
+  for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x) d[c] = s[c];
+  if (dst_scale && threadIdx.x == 0) dst_scale[r] = src_scale[t];
+}
+
+// Per-row E4M3 quantisation: s = amax / 448 (1 for an all-zero row), q = E4M3(v / s).
+// One wave per row; rows counted by *n_rows_dev when given (device-side row count).
+template <int IN>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int rows,
+                                                         const int32_t* __restrict__ n_rows_dev, int cols,
+                                                         uint8_t* __restrict__ dst, float* __restrict__ scale) {
+  const int r = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int n = n_rows_dev ? *n_rows_dev : rows;
+  if (r >= n) return;
+  // each lane handles 8 consecutive values per step
+  float amax = 0.0f;
+  for (int c = lane * 8; c < cols; c += kWave * 8) {
+    float v[8];
+    if (IN == EL_BF16) {
+      const uint4 p = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + static_cast<size_t>(r) * cols + c);
+      const uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_bits_to_f32(wds[q] & 0xFFFFu);
+        v[2 * q + 1] = bf16_bits_to_f32(wds[q] >> 16);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + static_cast<size_t>(r) * cols + c);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  }
+  amax = wave_max(amax);
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  for (int c = lane * 8; c < cols; c += kWave * 8) {
+    float v[8];
+    if (IN == EL_BF16) {
+      const uint4 p = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + static_cast<size_t>(r) * cols + c);
+      const uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_bits_to_f32(wds[q] & 0xFFFFu);
+        v[2 * q + 1] = bf16_bits_to_f32(wds[q] >> 16);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + static_cast<size_t>(r) * cols + c);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    uint32_t packed4[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float a0 = fminf(fmaxf(v[4 * q + 0] / s, -448.0f), 448.0f);
+      float a1 = fminf(fmaxf(v[4 * q + 1] / s, -448.0f), 448.0f);
+      float a2 = fminf(fmaxf(v[4 * q + 2] / s, -448.0f), 448.0f);
+      float a3 = fminf(fmaxf(v[4 * q + 3] / s, -448.0f), 448.0f);
+      packed4[q] = f32x2_to_e4m3x2(a0, a1) | (f32x2_to_e4m3x2(a2, a3) << 16);
+    }
+    *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * cols + c) = make_uint2(packed4[0], packed4[1]);
+  }
+  if (lane == 0) scale[r] = s;
+}
+
+// Tile schedule: prefix[g] = sum over groups g' < g of ceil(rows_g' / bm), for two
+// tile heights at once.  One workgroup of 1024 threads (n_groups <= 1024).
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int n_groups,
+                                                           int bm0, int bm1, int32_t* __restrict__ prefix0,
+                                                           int32_t* __restrict__ prefix1) {
+  __shared__ int32_t p0[1024], p1[1024];
+  const int g = threadIdx.x;
+  int c0 = 0, c1 = 0;
+  if (g < n_groups) {
+    const int rows = offsets[g + 1] - offsets[g];
+    c0 = (rows + bm0 - 1) / bm0;
+    c1 = (rows + bm1 - 1) / bm1;
+  }
+  p0[g] = c0;
+  p1[g] = c1;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v0 = g >= o ? p0[g - o] : 0;
+    const int v1 = g >= o ? p1[g - o] : 0;
+    __syncthreads();
+    p0[g] += v0;
+    p1[g] += v1;
+    __syncthreads();
+  }
+  if (g < n_groups) {
+    prefix0[g + 1] = p0[g];
+    prefix1[g + 1] = p1[g];
+  }
+  if (g == 0) {
+    prefix0[0] = 0;
+    prefix1[0] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
+                          int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
+                          hipStream_t stream) {
+  const int n_pairs = T * k;
+  const int n_units = perm_units(T, k);
+  const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
+  int n_bits = 1;
+  while ((1 << n_bits) < n_local) ++n_bits;
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
+                     n_units, hist);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, base, counts,
+                     offsets);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin,
+                     n_local, n_bits, n_units, base, perm_token, inv_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, const float* src_scale, const int32_t* perm_token,
+                              const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,
+                              hipStream_t stream) {
+  if (max_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(max_rows), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(src), src_scale, perm_token, n_rows_dev, row_bytes,
+                     static_cast<uint8_t*>(dst), dst_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(int in_el, const void* src, int rows, const int32_t* n_rows_dev, int cols, void* dst,
+                             float* scale, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (in_el == EL_BF16)
+    hipLaunchKernelGGL(quant_rows_kernel<EL_BF16>, grid, dim3(256), 0, stream, src, rows, n_rows_dev, cols,
+                       static_cast<uint8_t*>(dst), scale);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<EL_F32>, grid, dim3(256), 0, stream, src, rows, n_rows_dev, cols,
+                       static_cast<uint8_t*>(dst), scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int bm1, int32_t* prefix0,
+                              int32_t* prefix1, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, n_groups, bm0, bm1, prefix0,
+                     prefix1);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,299 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Bars: routing ids, counts, offsets, permutation: bit-exact; routing weights within
+1e-6 of the oracle's fp64 weights (same fp32 logits); gathered rows and E4M3 codes
+bit-exact; layer output max|y - y_ref| <= tol * max|y_ref| with tol 1e-4 (fp32),
+1e-2 (bf16), 3e-2 (fp8).  Sizes span several tiles with ragged tails; the
+full-size workloads are checked on sampled tokens in test_gpu_full.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_route_amd as moe
+import synth
+from harness import dims_of, gpu_layer, logit_bound, oracle_layer, oracle_routing, rel_err, to_np, tolerance
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+# Layer configurations: (workload, seed)
+MID = {
+    # fp32 tiny layer of the pages' shape family
+    "tiny_fp32": synth.WORKLOADS["tiny_fp32"],
+    "mid_fp32": W("mid_fp32", T=100, D=128, E=12, top_k=3, I=64, I_shared=64, act="f32", w="f32", out="f32"),
+    # few rows per expert (16-row tiles), partial K block, 3 gate/up and 2 down N-tiles
+    "decode_like_bf16": W("decode_like_bf16", T=96, D=256, E=64, top_k=6, I=192, I_shared=128,
+                          act="bf16", w="bf16", out="bf16"),
+    # ~30 rows per expert (32-row tiles, ragged second tile), 2 K blocks
+    "mid_bf16": W("mid_bf16", T=300, D=512, E=40, top_k=4, I=192, I_shared=128, act="bf16", w="bf16", out="bf16"),
+    # fp32 output from bf16 operands
+    "mid_bf16_f32out": W("mid_bf16_f32out", T=128, D=256, E=16, top_k=2, I=128, I_shared=64,
+                         act="bf16", w="bf16", out="f32"),
+    # skewed popularity: a hot expert spanning many M-tiles and never-chosen experts
+    "skew_bf16": W("skew_bf16", T=512, D=256, E=32, top_k=4, I=128, I_shared=64, act="bf16", w="bf16", out="bf16",
+                   skew_alpha=0.8, skew_s=1.1, skew_empty=4),
+    # expert-parallel slice with the router on
+    "slice_bf16": W("slice_bf16", T=200, D=256, E=32, top_k=4, I=128, I_shared=0, act="bf16", w="bf16",
+                    out="bf16", expert_begin=16, n_local=8),
+    # fp8 slice with given routing
+    "slice_fp8": W("slice_fp8", T=256, D=512, E=32, top_k=4, I=128, I_shared=0, act="bf16", w="e4m3", out="bf16",
+                   expert_begin=8, n_local=8, routing_given=True),
+    "slice_fp8_f32out": W("slice_fp8_f32out", T=64, D=256, E=16, top_k=3, I=64, I_shared=0, act="bf16", w="e4m3",
+                          out="f32", expert_begin=0, n_local=16, routing_given=True),
+    # no renormalisation; k = 1
+    "norenorm_k1": W("norenorm_k1", T=77, D=128, E=8, top_k=1, I=64, I_shared=64, act="bf16", w="bf16",
+                     out="bf16", renormalize=False),
+    # k = E
+    "k_eq_E": W("k_eq_E", T=33, D=128, E=8, top_k=8, I=64, I_shared=0, act="bf16", w="bf16", out="bf16"),
+    # a single token
+    "one_token": W("one_token", T=1, D=256, E=16, top_k=4, I=128, I_shared=64, act="bf16", w="bf16", out="bf16"),
+}
+
+
+def _check_layer(wl, seed=0, shared=True):
+    inp = synth.make_inputs(wl, seed, "cpu")
+    g = gpu_layer(inp, shared=shared)
+    if not wl.routing_given:
+        x64, wr64 = synth.f64(inp.x), synth.f64(inp.w_router)
+        l_ref = oracle.router_logits(x64, wr64).astype(np.float64)
+        bound = logit_bound(x64, wr64, l_ref)
+        assert np.all(np.abs(g["logits"] - l_ref) <= bound), "router logits outside the fp32 accumulation bound"
+    ref = oracle_layer(inp, g["logits"], shared=shared)
+    ids_gpu, w_gpu = oracle.unpack_routing(g["packed"])
+    np.testing.assert_array_equal(ids_gpu, ref["ids"])
+    np.testing.assert_allclose(w_gpu, ref["weights"], rtol=0, atol=1e-6)
+    err = rel_err(g["y"], ref["y"])
+    tol = tolerance(wl)
+    assert err <= tol, f"{wl.name}: rel err {err:.3e} > {tol}"
+    return err
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_layer_forward_parity(name):
+    _check_layer(MID[name])
+
+
+@pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "tiny_fp32", "skew_bf16"])
+def test_layer_forward_parity_without_shared_expert(name):
+    """The shared expert dominates y; without it a routed-path error cannot hide under the tolerance."""
+    _check_layer(MID[name], seed=1, shared=False)
+
+
+def test_layer_forward_two_calls_reuse_workspace():
+    wl = MID["mid_bf16"]
+    inp = synth.make_inputs(wl, 3, "cpu")
+    ws = moe.workspace(dims_of(wl))
+    a = gpu_layer(inp, ws=ws)
+    b = gpu_layer(inp, ws=ws)
+    np.testing.assert_array_equal(a["y"], b["y"])           # deterministic
+    np.testing.assert_array_equal(a["packed"], b["packed"])
+
+
+def test_expert_parallel_slices_sum_to_full_layer():
+    """Eight slices run one after another sum to the full routed layer (what a reduce-scatter adds)."""
+    full = W("ep_full", T=256, D=256, E=64, top_k=4, I=128, I_shared=0, act="bf16", w="bf16", out="f32",
+             routing_given=True)
+    inp = synth.make_inputs(full, 5, "cpu")
+    y_full = gpu_layer(inp)["y"]
+    total = np.zeros_like(y_full)
+    for b in range(0, 64, 8):
+        wl = full.replace(expert_begin=b, n_local=8)
+        part = synth.LayerInputs(wl, inp.x, None, inp.w_gate[b:b + 8].contiguous(), inp.w_up[b:b + 8].contiguous(),
+                                 inp.w_down[b:b + 8].contiguous(), packed=inp.packed)
+        total += gpu_layer(part)["y"]
+    assert rel_err(total, y_full) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# moe_route
+# ---------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    # (T, E, k, kind, renormalize)
+    (1000, 512, 10, "normal", True),
+    (700, 512, 10, "ties", True),
+    (300, 100, 7, "normal", True),
+    (257, 1024, 32, "normal", True),
+    (64, 16, 2, "ties", False),
+    (129, 32, 32, "normal", True),
+    (50, 512, 10, "bias_inf", True),
+    (31, 8, 1, "ties", True),
+]
+
+
+@pytest.mark.parametrize("T,E,k,kind,renorm", ROUTE_CASES)
+def test_route_from_given_logits(T, E, k, kind, renorm):
+    rng = np.random.default_rng(T * 7 + E)
+    if kind == "ties":
+        logits = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 3.0], np.float32), size=(T, E))
+    else:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = None
+    if kind == "bias_inf":
+        bias = (rng.standard_normal(E) * 0.5).astype(np.float32)
+        bias[rng.choice(E, E // 4, replace=False)] = -np.inf
+    d = moe.make_dims(T, 64, E, k, 64, renormalize=renorm)
+    lg = torch.from_numpy(logits).cuda()
+    packed = torch.empty(T, 2, k, dtype=torch.int32, device="cuda")
+    moe.moe_route(d, None, None, lg, None if bias is None else torch.from_numpy(bias).cuda(), packed)
+    ids_gpu, w_gpu = oracle.unpack_routing(packed.cpu().numpy())
+    ids, w = oracle.route(logits, k, bias=bias, renormalize=renorm)
+    np.testing.assert_array_equal(ids_gpu, ids)
+    np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
+
+
+def test_route_with_router_projection_bf16():
+    T, D, E, k = 333, 512, 128, 6
+    rng = np.random.default_rng(1)
+    x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
+    wr = torch.from_numpy((rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)).to(torch.bfloat16)
+    d = moe.make_dims(T, D, E, k, 64)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    packed = torch.empty(T, 2, k, dtype=torch.int32, device="cuda")
+    moe.moe_route(d, x.cuda(), wr.cuda(), logits, None, packed)
+    x64, w64 = to_np(x), to_np(wr)
+    l_ref = oracle.router_logits(x64, w64).astype(np.float64)
+    lg = logits.cpu().numpy()
+    assert np.all(np.abs(lg - l_ref) <= logit_bound(x64, w64, l_ref))
+    ids, w = oracle.route(lg, k)
+    ids_gpu, w_gpu = oracle.unpack_routing(packed.cpu().numpy())
+    np.testing.assert_array_equal(ids_gpu, ids)
+    np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# moe_permute
+# ---------------------------------------------------------------------------
+
+PERM_CASES = [
+    # (T, k, E, begin, n_local, junk): junk adds out-of-range ids and repeats
+    (512, 10, 512, 0, 512, False),
+    (5000, 10, 512, 64, 64, False),
+    (3001, 4, 100, 0, 100, True),
+    (1, 1, 4, 0, 4, False),
+    (2049, 8, 1024, 0, 1024, False),
+    (777, 3, 16, 5, 1, True),
+]
+
+
+def _packed_blob(rng, T, k, E, junk):
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    if junk:
+        m = rng.random((T, k)) < 0.1
+        ids[m] = rng.integers(-3, E + 3, m.sum())
+    w = rng.random((T, k)).astype(np.float32)
+    return oracle.pack_routing(ids, w), ids
+
+
+@pytest.mark.parametrize("T,k,E,begin,n_local,junk", PERM_CASES)
+def test_permute_bit_exact(T, k, E, begin, n_local, junk):
+    rng = np.random.default_rng(T + k)
+    packed, ids = _packed_blob(rng, T, k, E, junk)
+    d = moe.make_dims(T, 64, E, k, 64, expert_begin=begin, n_local=n_local)
+    counts = torch.empty(n_local, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(n_local + 1, dtype=torch.int32, device="cuda")
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    ws = moe.workspace(d)
+    moe.moe_permute(d, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, ws=ws)
+    c, o, p, iv = oracle.permute(ids, begin, n_local)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    n_a = int(o[-1])
+    np.testing.assert_array_equal(perm.cpu().numpy()[:n_a], p)
+    np.testing.assert_array_equal(inv.cpu().numpy(), iv)
+
+
+def test_permute_gathers_rows_and_quantises_fp8():
+    T, k, E, D = 300, 4, 24, 256
+    rng = np.random.default_rng(2)
+    packed, ids = _packed_blob(rng, T, k, E, False)
+    x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
+    x[7] = 0                                                 # an all-zero token: scale 1
+    # bf16 gather: permute then unpermute is the identity
+    d = moe.make_dims(T, D, E, k, 64)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    xp = torch.empty(T * k, D, dtype=torch.bfloat16, device="cuda")
+    moe.moe_permute(d, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, x.cuda(), xp, None,
+                    ws=moe.workspace(d))
+    xp_h, inv_h = xp.cpu(), inv.cpu().numpy()
+    for t in range(T):
+        for j in range(k):
+            assert torch.equal(xp_h[inv_h[t, j]], x[t])
+    # fp8 gather: per-token E4M3 codes and scales, bit-exact against the oracle's quantiser
+    d8 = moe.make_dims(T, D, E, k, 64, w="e4m3")
+    xq = torch.empty(T * k, D, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    moe.moe_permute(d8, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, x.cuda(), xq, xs,
+                    ws=moe.workspace(d8))
+    q_ref, s_ref = oracle.quantize_rows_e4m3(to_np(x))
+    codes_ref = oracle.e4m3_encode(q_ref)
+    c, o, p, iv = oracle.permute(ids, 0, E)
+    n_a = int(o[-1])
+    np.testing.assert_array_equal(xq.cpu().numpy()[:n_a], codes_ref[p])
+    np.testing.assert_array_equal(xs.cpu().numpy()[:n_a], s_ref[p])
+
+
+# ---------------------------------------------------------------------------
+# moe_grouped_ffn and moe_unpermute_combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "mid_fp32"])
+def test_grouped_ffn_gather_and_grouped_rows_agree_with_oracle(name):
+    wl = MID[name]
+    inp = synth.make_inputs(wl, 4, "cpu")
+    dev = inp.to("cuda")
+    rng = np.random.default_rng(4)
+    packed, ids = _packed_blob(rng, wl.T, wl.top_k, wl.E, False)
+    d = dims_of(wl, shared=False)
+    ws = moe.workspace(d)
+    T, k, D = wl.T, wl.top_k, wl.D
+    counts = torch.empty(wl.local, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(wl.local + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    xp = torch.empty(T * k, D, dtype=dev.x.dtype, device="cuda")
+    moe.moe_permute(d, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, dev.x, xp, None, ws=ws)
+    out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
+    out_a = torch.empty(T * k, D, dtype=out_dt, device="cuda")
+    out_b = torch.empty(T * k, D, dtype=out_dt, device="cuda")
+    moe.moe_grouped_ffn(d, dev.x, None, perm, offsets, dev.w_gate, dev.w_up, dev.w_down, None, None, None, out_a, ws)
+    moe.moe_grouped_ffn(d, xp, None, None, offsets, dev.w_gate, dev.w_up, dev.w_down, None, None, None, out_b, ws)
+    torch.cuda.synchronize()
+    n_a = int(offsets[-1].item())
+    a, b = to_np(out_a[:n_a]), to_np(out_b[:n_a])
+    np.testing.assert_array_equal(a, b)                      # same sums in the same order
+    c, o, p, iv = oracle.permute(ids, 0, wl.local)
+    x64 = synth.f64(inp.x)
+    ev = synth.ExpertView(inp)
+    ref = np.zeros((n_a, D))
+    for e in range(wl.local):
+        if o[e] < o[e + 1]:
+            ref[o[e]:o[e + 1]] = oracle.swiglu_expert(x64[p[o[e]:o[e + 1]]], *ev[e])
+    assert rel_err(a, ref) <= tolerance(wl)
+    # combine the grouped outputs
+    y = torch.empty(T, D, dtype=out_dt, device="cuda")
+    moe.moe_unpermute_combine(d, out_a, torch.from_numpy(packed).cuda(), inv, None, y)
+    _, w32 = oracle.unpack_routing(packed)
+    y_ref = oracle.combine(a, w32.astype(np.float64), iv)    # same (rounded) rows: only the sum is checked
+    np.testing.assert_allclose(to_np(y), y_ref, rtol=0, atol=(1e-6 if wl.out == "f32" else 2 ** -8) * np.abs(y_ref).max())
+
+
+def test_shared_expert_alone_through_grouped_ffn():
+    wl = MID["mid_bf16"]
+    inp = synth.make_inputs(wl, 6, "cpu")
+    dev = inp.to("cuda")
+    d = moe.make_dims(wl.T, wl.D, 1, 1, wl.I_shared, act="bf16", w="bf16", out="bf16")
+    offsets = torch.tensor([0, wl.T], dtype=torch.int32, device="cuda")
+    out = torch.empty(wl.T, wl.D, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_ffn(d, dev.x, None, None, offsets, dev.ws_gate, dev.ws_up, dev.ws_down, None, None, None, out,
+                        moe.workspace(d))
+    ref = oracle.swiglu_expert(synth.f64(inp.x), *synth.shared_f64(inp))
+    assert rel_err(to_np(out), ref) <= 1e-2

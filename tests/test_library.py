@@ -1,0 +1,137 @@
+"""Host-side checks of the C-ABI library (no GPU, no kernel launches).
+
+The library must load, export every entry point that include/moe.h declares,
+size its workspace, and reject bad arguments on the host before touching the
+GPU (every call here fails validation, so nothing is launched).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_ffn_route_amd as moe
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = moe.library()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.moe_abi_version() == 1
+
+
+def test_library_targets_gfx950_only():
+    blob = open(moe.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in blob
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workspace_bytes_for_every_workload(name):
+    wl = synth.WORKLOADS[name]
+    n = moe.moe_workspace_bytes(moe.make_dims(wl.T, wl.D, wl.E, wl.top_k, wl.I, wl.I_shared, wl.expert_begin,
+                                              wl.local, True, wl.act, wl.w, wl.out))
+    tk = wl.T * wl.top_k
+    out_b = 4 if wl.out == "f32" else 2
+    assert n >= tk * wl.D * out_b          # at least the grouped expert outputs
+    assert n % 256 == 0
+    assert n < 4 * 2 ** 30
+
+
+def _dims(**kw):
+    base = dict(T=8, D=64, E=8, top_k=2, I=64, I_shared=0, expert_begin=0, n_local=None, renormalize=True,
+                act="bf16", w="bf16", out="bf16")
+    base.update(kw)
+    return moe.make_dims(**base)
+
+
+BAD_DIMS = [dict(T=-1), dict(D=0), dict(E=0), dict(top_k=0), dict(top_k=9), dict(I=0), dict(I_shared=-64),
+            dict(expert_begin=6, n_local=4), dict(expert_begin=-1, n_local=2)]
+UNSUPPORTED = [dict(D=96), dict(I=100), dict(I_shared=32), dict(E=2048, top_k=2), dict(E=64, top_k=33),
+               dict(act="f32", w="bf16"), dict(act="f32", w="f32", out="bf16"), dict(act="bf16", w="f32"),
+               dict(act="e4m3", w="e4m3")]
+
+
+@pytest.mark.parametrize("kw", BAD_DIMS)
+def test_bad_dims_rejected(kw):
+    assert moe.moe_workspace_bytes(_dims(**kw)) == 0
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None)
+    assert st == moe.ERR_BAD_DIMS
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED)
+def test_unsupported_rejected(kw):
+    assert moe.moe_workspace_bytes(_dims(**kw)) == 0
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None)
+    assert st == moe.ERR_UNSUPPORTED
+
+
+def test_null_arguments_rejected():
+    lib = moe.library()
+    d = _dims()
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_workspace_bytes(None) == 0
+    assert lib.moe_route(None, None, None, fake, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, fake, None) == moe.ERR_NULL_ARG
+    # x without a router weight
+    assert lib.moe_route(ctypes.byref(d), fake, None, fake, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_permute(ctypes.byref(d), None, fake, fake, fake, fake, None, None, None, fake, 1 << 20,
+                           None) == moe.ERR_NULL_ARG
+    assert lib.moe_unpermute_combine(ctypes.byref(d), fake, fake, None, None, fake, None) == moe.ERR_NULL_ARG
+    w = moe.moe_weights(None, fake, fake, fake, None, None, None, None, None, None)
+    # neither a router weight nor a given routing
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake,
+                                 1 << 30, None) == moe.ERR_NULL_ARG
+    # fp8 weights without scales
+    d8 = _dims(w="e4m3")
+    assert lib.moe_grouped_ffn(ctypes.byref(d8), fake, fake, None, fake, fake, fake, fake, None, None, None, fake,
+                               fake, 1 << 30, None) == moe.ERR_NULL_ARG
+
+
+def test_small_workspace_rejected():
+    lib = moe.library()
+    d = _dims()
+    need = moe.moe_workspace_bytes(d)
+    fake = ctypes.c_void_p(256)
+    st = lib.moe_permute(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, None, fake, need - 1, None)
+    assert st == moe.ERR_WORKSPACE
+    w = moe.moe_weights(fake, fake, fake, fake, None, None, None, None, None, None)
+    st = lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake, need - 1,
+                               None)
+    assert st == moe.ERR_WORKSPACE
+
+
+def test_zero_tokens_is_a_no_op():
+    lib = moe.library()
+    d = _dims(T=0)
+    need = moe.moe_workspace_bytes(d)
+    fake = ctypes.c_void_p(256)
+    w = moe.moe_weights(fake, fake, fake, fake, None, None, None, None, None, None)
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake, need,
+                                 None) == moe.OK
+    assert lib.moe_route(ctypes.byref(d), None, None, fake, None, fake, None) == moe.OK
+
+
+def test_status_strings():
+    lib = moe.library()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.moe_status_string(code)
+    assert lib.moe_last_hip_error() == 0
