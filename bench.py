@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN layer on one MI355X.
+
+One step = one pass of the whole layer (router GEMM, top-k routing, grouping by
+expert, grouped gate/up SwiGLU GEMM with the shared expert, grouped down GEMM,
+weighted combine) over one batch, through the C-ABI entry moe_layer_forward.
+Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM before
+the timed region.  The primary line is the 512-token decode batch (D=4096,
+512 experts of I=1024, top-10, one shared expert of I=1024, bf16); the
+8192-token prefill chunk of the same layer is measured in the same run.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the grouped
+gate/up GEMM), timed live with HIP events recorded on the launch stream around
+it in every timed step; `cpu_baseline` times the CPU oracle on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # dense fp8 MFMA
+METRIC = "MoE-layer tokens/sec on 1 MI355X (T=512 decode, T=8192 prefill) + % roofline"
+_ES = {"f32": 4, "bf16": 2, "e4m3": 1}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode_bf16")
+    p.add_argument("--secondary", default="prefill_bf16",
+                   help="second workload measured with the same weights ('' to skip)")
+    p.add_argument("--secondary-steps", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens of the oracle sample (0: whole batch)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (calibrates HBM counters)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the sources of the timed kernels (traffic figures are void once these change)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_ffn_route_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, if it matches these kernels."""
+    path = os.path.join(ROOT, "profiles", f"gemm_gate_up_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_hash:\s*`?([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*`?([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+class Layer:
+    """Buffers and launch of one workload (device inputs shared with another workload when given)."""
+
+    def __init__(self, wl, inp):
+        import torch
+        import sparse_moe_ffn_route_amd as moe
+        self.torch, self.moe, self.wl, self.inp = torch, moe, wl, inp
+        self.dims = moe.make_dims(wl.T, wl.D, wl.E, wl.top_k, wl.I, wl.I_shared, wl.expert_begin, wl.local,
+                                  wl.renormalize, wl.act, wl.w, wl.out)
+        self.ws = moe.workspace(self.dims)
+        out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
+        self.y = torch.empty(wl.T, wl.D, dtype=out_dt, device="cuda")
+        self.logits = None if wl.routing_given else torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
+        self.packed = torch.empty(wl.T, 2, wl.top_k, dtype=torch.int32, device="cuda")
+        sh = wl.I_shared > 0
+        self.weights = moe.make_weights(inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
+                                        inp.s_down, inp.ws_gate if sh else None, inp.ws_up if sh else None,
+                                        inp.ws_down if sh else None)
+
+    def step(self, events=None):
+        self.moe.moe_layer_forward(self.dims, self.weights, self.inp.x, self.inp.packed, self.inp.bias, self.y,
+                                   self.logits, self.packed, self.ws, stage_events=events)
+
+    def new_events(self):
+        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(self.moe.STAGE_EVENTS)]
+        for e in evs:
+            e.record()       # torch creates the underlying hipEvent on first record
+        return evs
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        ev_sets = [self.new_events() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(ev_sets[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stages = {name: [] for name in self.moe.STAGES}
+        for evs in ev_sets:
+            for j, name in enumerate(self.moe.STAGES):
+                stages[name].append(evs[j].elapsed_time(evs[j + 1]))
+        return wall, {k: sum(v) / len(v) for k, v in stages.items()}
+
+    # ---- algorithmic work ---------------------------------------------------
+    def routing_stats(self):
+        torch = self.torch
+        ids = self.packed[:, 0, :].reshape(-1).long() - self.wl.expert_begin
+        ids = ids[(ids >= 0) & (ids < self.wl.local)]
+        counts = torch.bincount(ids, minlength=self.wl.local)
+        return int(ids.numel()), int((counts > 0).sum().item()), counts
+
+    def work(self):
+        wl = self.wl
+        n_a, active, counts = self.routing_stats()
+        wb, ab = _ES[wl.w], _ES[wl.act]
+        hb = 4 if wl.act == "f32" else 2
+        ob = _ES[wl.out]
+        scales = (2 * wl.I + wl.D) * 4 if wl.w == "e4m3" else 0
+        expert_w = active * (3 * wl.D * wl.I * wb + scales)
+        shared_w = 3 * wl.D * wl.I_shared * ab
+        router_w = 0 if wl.routing_given else wl.E * wl.D * ab
+        io = wl.T * wl.D * ab + wl.T * wl.D * ob + wl.T * 2 * wl.top_k * 4
+        layer_bytes = expert_w + shared_w + router_w + io
+        layer_flop = (0 if wl.routing_given else 2 * wl.T * wl.D * wl.E) + n_a * 6 * wl.D * wl.I \
+            + wl.T * 6 * wl.D * wl.I_shared
+        # gate/up kernel: gate+up weights of every active expert and of the shared expert,
+        # x read once, h written once
+        gu_bytes = active * (2 * wl.D * wl.I * wb + (2 * wl.I * 4 if wl.w == "e4m3" else 0)) \
+            + 2 * wl.D * wl.I_shared * ab + wl.T * wl.D * ab + n_a * wl.I * hb + wl.T * wl.I_shared * hb
+        gu_flop = n_a * 4 * wl.D * wl.I + wl.T * 4 * wl.D * wl.I_shared
+        return dict(n_assign=n_a, active_experts=active, max_rows=int(counts.max().item()),
+                    layer_bytes=layer_bytes, layer_flop=layer_flop, gate_up_bytes=gu_bytes, gate_up_flop=gu_flop)
+
+
+def layer_summary(layer, wall, stages, steps):
+    wl = layer.wl
+    w = layer.work()
+    ms = wall / steps * 1e3
+    peak_tf = FP8_PEAK_TFLOPS if wl.w == "e4m3" else BF16_PEAK_TFLOPS
+    hbm_frac = w["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    mfma_frac = w["layer_flop"] / (ms * 1e-3) / 1e12 / peak_tf
+    return dict(workload=wl.name, tokens_per_s=wl.T / (ms * 1e-3), ms_per_step=ms,
+                layer_hbm_frac=hbm_frac, layer_mfma_frac=mfma_frac,
+                layer_roofline_frac=max(hbm_frac, mfma_frac), stage_ms=stages, work=w)
+
+
+def roofline_of(layer, stages):
+    w = layer.work()
+    t = stages["gate_up"] * 1e-3
+    achieved = w["gate_up_bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(layer.wl.name),
+            "kernel": "gemm_kernel<bf16,SwiGLU> (grouped gate/up + shared expert)",
+            "bytes_per_launch": w["gate_up_bytes"], "avg_launch_ms": round(stages["gate_up"], 4)}
+
+
+def cpu_baseline(layer, sample_tokens):
+    """The oracle, as it stands, on the host cores: routing from the GPU's fp32 logits, then the layer."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    import oracle
+    import synth
+    wl, inp = layer.wl, layer.inp
+    T = wl.T if sample_tokens <= 0 else min(sample_tokens, wl.T)
+    cores = len(os.sched_getaffinity(0))
+    # host copies of the stored inputs (not timed)
+    host = synth.LayerInputs(wl, inp.x[:T].cpu(), None, inp.w_gate.cpu(), inp.w_up.cpu(), inp.w_down.cpu(),
+                             None if inp.s_gate is None else inp.s_gate.cpu(),
+                             None if inp.s_up is None else inp.s_up.cpu(),
+                             None if inp.s_down is None else inp.s_down.cpu(),
+                             None if inp.ws_gate is None else inp.ws_gate.cpu(),
+                             None if inp.ws_up is None else inp.ws_up.cpu(),
+                             None if inp.ws_down is None else inp.ws_down.cpu())
+    logits = None if layer.logits is None else layer.logits[:T].cpu().numpy()
+    packed = layer.packed[:T].cpu().numpy()
+    bias = None if inp.bias is None else inp.bias.cpu().numpy()
+    x64 = synth.f64(host.x)
+    torch.set_num_threads(cores)
+    with threadpoolctl.threadpool_limits(cores):
+        t0 = time.perf_counter()
+        if wl.routing_given:
+            ids, w32 = oracle.unpack_routing(packed)
+            w = w32.astype(np.float64)
+        else:
+            ids, w = oracle.route(logits, wl.top_k, bias=bias, renormalize=wl.renormalize)
+        if wl.w == "e4m3":
+            oracle.layer_from_routing_fp8(x64, ids, w, synth.ExpertViewFP8(host), expert_begin=wl.expert_begin,
+                                          n_local=wl.local)
+        else:
+            oracle.layer_from_routing(x64, ids, w, synth.ExpertView(host), shared=synth.shared_f64(host),
+                                      expert_begin=wl.expert_begin, n_local=wl.local)
+        dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {T} tokens of the {wl.name} batch (T={wl.T}): fp64 NumPy oracle, routing from the "
+                      f"GPU's fp32 logits, grouped experts, combine; {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * 2 ** 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this layer is built and measured on one GPU; --gpus must be 1 "
+                                   "(expert-parallel sharding across GPUs is a design note, not a run mode)"}))
+        return 2
+
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+
+    wl = synth.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(wl, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] inputs for {wl.name} drawn on the GPU in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    layer = Layer(wl, inp)
+    wall, stages = layer.run(args.steps, args.warmup)
+    prim = layer_summary(layer, wall, stages, args.steps)
+    print(f"[bench] {wl.name}: {prim['ms_per_step']:.3f} ms/step, stages {stages}", file=sys.stderr, flush=True)
+
+    secondary = []
+    if args.secondary:
+        wl2 = synth.WORKLOADS[args.secondary]
+        same_layer = all(getattr(wl2, f) == getattr(wl, f) for f in ("D", "E", "I", "I_shared", "w", "act"))
+        if same_layer:
+            # same weights; new hidden states of the secondary batch size
+            g = torch.Generator(device="cuda")
+            g.manual_seed(synth._torch_seed(0, "x", 1))
+            x2 = (torch.randn(wl2.T, wl2.D, generator=g, device="cuda")).to(torch.bfloat16)
+            inp2 = synth.LayerInputs(wl2, x2, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
+                                     inp.s_down, inp.ws_gate, inp.ws_up, inp.ws_down, None, None)
+            layer2 = Layer(wl2, inp2)
+            wall2, stages2 = layer2.run(args.secondary_steps, 2)
+            sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
+            sec["roofline"] = roofline_of(layer2, stages2)
+            secondary.append(sec)
+            print(f"[bench] {wl2.name}: {sec['ms_per_step']:.3f} ms/step, stages {stages2}", file=sys.stderr,
+                  flush=True)
+            del layer2, inp2, x2
+
+    probe = copy_probe(args.copy_probe_mib) if args.copy_probe_mib else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(layer, args.cpu_sample_tokens)
+        print(f"[bench] oracle: {cpu['seconds']} s", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(prim["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.w if wl.w == "e4m3" else wl.act,
+        "data": "synthetic (seeded Philox draws on the GPU; random-init weights)",
+        "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "E": wl.E, "top_k": wl.top_k, "I": wl.I,
+                   "I_shared": wl.I_shared, "expert_slice": [wl.expert_begin, wl.local], "parallelism": "1 GPU"},
+        "roofline": roofline_of(layer, stages),
+        "cpu_baseline": cpu,
+        "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_roofline_frac", "stage_ms")},
+        "work": prim["work"],
+        "secondary": secondary,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if probe:
+        out["copy_probe"] = probe
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -190,10 +190,17 @@ int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int3
  *              (zero rows for tokens without a local expert).
  *   logits_out [T][E] fp32 or NULL: copy of the router logits
  *   packed_out [T][2][top_k] int32 or NULL: copy of the routing blob
+ *   stage_events NULL, or MOE_STAGE_EVENTS caller-created hipEvent_t handles (as
+ *              void*) that are recorded on `stream` at the stage boundaries: [0] before
+ *              routing, [1] after routing, [2] after grouping (and the fp8 quantisation
+ *              of x), [3] after the gate/up GEMM, [4] after the down GEMM, [5] after the
+ *              combine.  Only for timing; the kernels are the same either way.
  */
+#define MOE_STAGE_EVENTS 6
 int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const void* x,
                       const int32_t* packed_in, const float* logit_bias, void* y, float* logits_out,
-                      int32_t* packed_out, void* ws, size_t ws_bytes, void* stream);
+                      int32_t* packed_out, void* ws, size_t ws_bytes, void* const* stage_events,
+                      void* stream);
 
 /* Human-readable text of a moe_status code (static storage). */
 const char* moe_status_string(int status);

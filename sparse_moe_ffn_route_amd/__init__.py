@@ -74,7 +74,7 @@ def library() -> ctypes.CDLL:
     lib.moe_grouped_ffn.restype = i32
     lib.moe_unpermute_combine.argtypes = [dp, vp, vp, vp, vp, vp, vp]
     lib.moe_unpermute_combine.restype = i32
-    lib.moe_layer_forward.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_layer_forward.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.moe_layer_forward.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -163,11 +163,22 @@ def make_weights(w_router=None, w_gate=None, w_up=None, w_down=None, s_gate=None
                                            sh_gate, sh_up, sh_down)])
 
 
+STAGE_EVENTS = 6   # MOE_STAGE_EVENTS
+STAGES = ("route", "permute", "gate_up", "down", "combine")
+
+
 def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, logits_out=None, packed_out=None,
-                      ws=None, stream=None):
+                      ws=None, stage_events=None, stream=None):
+    """stage_events: None or STAGE_EVENTS recorded torch.cuda.Event(enable_timing=True) objects."""
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
+        ev = (ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
     _check(library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _ptr(packed_in),
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
-                                       ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_forward")
+                                       ws.numel() if ws is not None else 0, ev, _stream(stream)),
+           "moe_layer_forward")
 
 
 def torch_dtype(code: int) -> torch.dtype:

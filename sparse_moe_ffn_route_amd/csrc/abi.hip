@@ -131,7 +131,8 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                     const int32_t* perm, const int32_t* offsets, const void* w_gate, const void* w_up,
                     const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
                     void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
-                    const void* sh_down, void* sh_out, hipStream_t s) {
+                    const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
+                    hipStream_t s) {
   const int mf = choose_mf(d);
   const int bm = gemm_bm(mf);
   const int tk = d.T * d.top_k;
@@ -144,7 +145,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   const int hel = h_el(d);
   const bool shared = d.I_shared > 0 && sh_gate;
 
-  MOE_TRY(launch_tile_prefix(offsets, d.n_local, bm, bm, tp_a, tp_b, s));
+  if (!have_tile_prefix) MOE_TRY(launch_tile_prefix(offsets, d.n_local, bm, bm, tp_a, tp_b, s));
 
   // gate/up with the fused SwiGLU epilogue
   const GemmProblem g0 = problem(a_rows, perm, a_scale, d.D, offsets, tp_a, d.n_local, 0, w_gate, w_up, s_gate, s_up,
@@ -162,6 +163,8 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
       MOE_TRY(launch_gemm(d.act_dtype, hel, true, mf, gs, nullptr,
                           ((d.T + bm - 1) / bm) * ((d.I_shared + kBnSwiglu - 1) / kBnSwiglu), s));
   }
+
+  if (ev_gate_up) MOE_TRY(hipEventRecord(ev_gate_up, s));
 
   // down projection of every grouped row
   const void* h_in = h;
@@ -261,7 +264,8 @@ int moe_grouped_ffn(const moe_dims* dims, const void* a_rows, const float* a_sca
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
   return experts_forward(d, ws, L, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
+                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr,
+                         static_cast<hipStream_t>(stream));
 }
 
 int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,
@@ -277,7 +281,7 @@ int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int3
 
 int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x, const int32_t* packed_in,
                       const float* logit_bias, void* y, float* logits_out, int32_t* packed_out, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      size_t ws_bytes, void* const* stage_events, void* stream) {
   int st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims& d = *dims;
@@ -291,6 +295,10 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) : hipSuccess;
+  };
+  MOE_TRY(mark(0));
 
   // 1. routing
   const int32_t* packed = packed_in;
@@ -306,15 +314,17 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
                            hipMemcpyDeviceToDevice, s));
   }
 
-  // 2. grouping by expert
+  MOE_TRY(mark(1));
+
+  // 2. grouping by expert (and the tile schedule of both grouped GEMMs)
   int32_t* counts = at<int32_t>(ws, L.counts);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm_token);
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
                          at<int32_t>(ws, L.base), counts, offsets, perm, inv, s));
-
-  // 3. experts (+ shared)
+  const int bm = gemm_bm(choose_mf(d));
+  MOE_TRY(launch_tile_prefix(offsets, d.n_local, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
   const void* a_rows = x;
   const float* a_scale = nullptr;
   if (fp8) {
@@ -322,14 +332,20 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
     a_rows = at<void>(ws, L.xq);
     a_scale = at<float>(ws, L.sx);
   }
+  MOE_TRY(mark(2));
+
+  // 3. experts (+ shared)
   void* out_rows = at<void>(ws, L.out_rows);
   void* sh_out = d.I_shared ? at<void>(ws, L.sh_out) : nullptr;
   st = experts_forward(d, ws, L, a_rows, a_scale, perm, offsets, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up,
-                       w->s_down, out_rows, x, d.I_shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, sh_out, s);
+                       w->s_down, out_rows, x, d.I_shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, sh_out, true,
+                       stage_events ? static_cast<hipEvent_t>(stage_events[3]) : nullptr, s);
   if (st != MOE_OK) return st;
+  MOE_TRY(mark(4));
 
   // 4. unpermute + weighted combine (+ shared)
-  return hip_status(launch_combine(d.out_dtype, out_rows, packed, inv, sh_out, d.T, d.D, d.top_k, y, s));
+  MOE_TRY(launch_combine(d.out_dtype, out_rows, packed, inv, sh_out, d.T, d.D, d.top_k, y, s));
+  return hip_status(mark(5));
 }
 
 const char* moe_status_string(int status) {

@@ -99,7 +99,7 @@ def test_null_arguments_rejected():
     w = moe.moe_weights(None, fake, fake, fake, None, None, None, None, None, None)
     # neither a router weight nor a given routing
     assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake,
-                                 1 << 30, None) == moe.ERR_NULL_ARG
+                                 1 << 30, None, None) == moe.ERR_NULL_ARG
     # fp8 weights without scales
     d8 = _dims(w="e4m3")
     assert lib.moe_grouped_ffn(ctypes.byref(d8), fake, fake, None, fake, fake, fake, fake, None, None, None, fake,
@@ -115,7 +115,7 @@ def test_small_workspace_rejected():
     assert st == moe.ERR_WORKSPACE
     w = moe.moe_weights(fake, fake, fake, fake, None, None, None, None, None, None)
     st = lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake, need - 1,
-                               None)
+                               None, None)
     assert st == moe.ERR_WORKSPACE
 
 
@@ -126,7 +126,7 @@ def test_zero_tokens_is_a_no_op():
     fake = ctypes.c_void_p(256)
     w = moe.moe_weights(fake, fake, fake, fake, None, None, None, None, None, None)
     assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake, need,
-                                 None) == moe.OK
+                                 None, None) == moe.OK
     assert lib.moe_route(ctypes.byref(d), None, None, fake, None, fake, None) == moe.OK
 
 
