@@ -120,9 +120,12 @@ size_t moe_workspace_bytes(const moe_dims* dims);
  *   logit_bias [E] fp32 or NULL (an additive popularity bias; -inf never chosen).
  *              Each token needs at least top_k finite keys; NaN is not supported.
  *   packed     [T][2][top_k] int32 output.
+ *   ws         scratch of ws_bytes >= moe_workspace_bytes(dims), or NULL.  With scratch, a
+ *              small-T projection is split along D into partial products that the
+ *              routing kernel adds in a fixed order (same result on every call).
  */
 int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* logits,
-              const float* logit_bias, int32_t* packed, void* stream);
+              const float* logit_bias, int32_t* packed, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Permutation: group the (token, slot) pairs whose expert is local by expert

@@ -66,7 +66,7 @@ def library() -> ctypes.CDLL:
     dp, wp = ctypes.POINTER(moe_dims), ctypes.POINTER(moe_weights)
     lib.moe_workspace_bytes.argtypes = [dp]
     lib.moe_workspace_bytes.restype = sz
-    lib.moe_route.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
@@ -131,9 +131,10 @@ def workspace(dims: moe_dims, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def moe_route(dims, x, w_router, logits, logit_bias, packed, stream=None):
+def moe_route(dims, x, w_router, logits, logit_bias, packed, ws=None, stream=None):
     _check(library().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(logit_bias),
-                               _ptr(packed), _stream(stream)), "moe_route")
+                               _ptr(packed), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_route")
 
 
 def moe_permute(dims, packed, counts, offsets, perm_token, inv_pos, x=None, x_perm=None, x_perm_scale=None,

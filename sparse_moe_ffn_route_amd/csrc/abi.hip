@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,8 +40,25 @@ int check_dims(const moe_dims* d) {
   return MOE_OK;
 }
 
+// Shape of the router projection: 32-row streaming tiles (E / 128 N-tiles per 32 tokens
+// already fill the chip at prefill sizes; small T is split along D instead).
+int router_shape(const moe_dims&) { return kShapeStream32; }
+
+// K splits of the router projection: enough workgroups to cover the chip when T is
+// small (decode), none when the M x N tiles already do (prefill).
+int router_splits(const moe_dims& d) {
+  const int row_bytes = d.D * act_size(d.act_dtype);
+  if (row_bytes % 512) return 1;
+  const int blocks = row_bytes / 512;
+  const int bm = gemm_bm(router_shape(d)), bn = gemm_bn(false, router_shape(d));
+  const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn);
+  int s = 1;
+  while (s * 2 <= blocks && blocks % (s * 2) == 0 && static_cast<int64_t>(tiles) * s * 2 <= 512) s *= 2;
+  return s;
+}
+
 struct Layout {
-  size_t logits, packed, hist, base, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
+  size_t logits, logits_part, packed, hist, base, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
   size_t xq, sx, h, h_sh, hq, sh, out_rows, sh_out, total;
 };
 
@@ -58,6 +75,8 @@ Layout layout(const moe_dims& d) {
   const bool fp8 = d.w_dtype == MOE_E4M3;
   const size_t hs = act_size(d.act_dtype), os = out_size(d.out_dtype);
   L.logits = take(T * d.E * 4);
+  const int rs = router_splits(d);
+  L.logits_part = take(rs > 1 ? static_cast<size_t>(rs) * T * d.E * 4 : 0);
   L.packed = take(tk * 2 * 4);
   L.hist = take(nl * U * 4);
   L.base = take(nl * U * 4);
@@ -93,18 +112,16 @@ int hip_status(hipError_t e) {
     if (_s != MOE_OK) return _s;             \
   } while (0)
 
-// Tiles per M-row fragment count: average routed rows per expert decides.
-int choose_mf(const moe_dims& d) {
+// Shape of the grouped expert GEMMs: the average routed rows per expert decides.
+int expert_shape(const moe_dims& d) {
   const double avg = static_cast<double>(d.T) * d.top_k / d.E;
-  return avg <= 16.0 ? 1 : 2;
+  return avg <= 16.0 ? kShapeStream16 : avg <= 32.0 ? kShapeStream32 : kShapeTile256;
 }
 
 int routed_tile_bound(int rows_total, int n_groups, int bm, int n, int bn) {
   const int64_t mt = (static_cast<int64_t>(rows_total) + static_cast<int64_t>(n_groups) * (bm - 1)) / bm;
   return static_cast<int>(mt * ((n + bn - 1) / bn));
 }
-
-constexpr int kBnSwiglu = 64, kBnPlain = 128;
 
 GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, int lda, const int32_t* offsets,
                     const int32_t* tile_prefix, int n_groups, int rows, const void* w0, const void* w1,
@@ -114,15 +131,26 @@ GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, in
   p.offsets = offsets; p.tile_prefix = tile_prefix; p.n_groups = n_groups; p.rows = rows;
   p.w0 = w0; p.w1 = w1; p.s0 = s0; p.s1 = s1; p.w_stride = w_stride;
   p.out = out; p.ldo = ldo; p.N = N; p.K = K;
+  p.k_splits = 1; p.out_split_stride = 0;
   return p;
 }
 
-int router_logits(const moe_dims& d, const void* x, const void* w_router, float* logits, hipStream_t s) {
-  const GemmProblem p = problem(x, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, w_router, nullptr, nullptr,
-                                nullptr, 0, logits, d.E, d.E, d.D);
-  const int mf = 2;
-  const int tiles = ((d.T + 16 * mf - 1) / (16 * mf)) * ((d.E + kBnPlain - 1) / kBnPlain);
-  return hip_status(launch_gemm(d.act_dtype, EL_F32, false, mf, p, nullptr, tiles, s));
+// Router projection + top-k.  parts: scratch for split-K partial products (NULL: no split).
+int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* logits, float* parts,
+                 const float* bias, int32_t* packed, hipStream_t s) {
+  if (x) {
+    const int splits = parts ? router_splits(d) : 1;
+    GemmProblem p = problem(x, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, w_router, nullptr, nullptr, nullptr,
+                            0, splits > 1 ? parts : logits, d.E, d.E, d.D);
+    p.k_splits = splits;
+    p.out_split_stride = static_cast<long long>(d.T) * d.E;
+    const int shape = router_shape(d);
+    const int bm = gemm_bm(shape), bn = gemm_bn(false, shape);
+    const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn) * splits;
+    MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, p, nullptr, tiles, s));
+    return hip_status(launch_route(parts, splits, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
+  }
+  return hip_status(launch_route(nullptr, 1, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
 }
 
 // gate/up -> h (+ quantise) -> down for the routed groups, with an optional shared
@@ -133,8 +161,9 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                     void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
                     const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
                     hipStream_t s) {
-  const int mf = choose_mf(d);
-  const int bm = gemm_bm(mf);
+  const int shape = expert_shape(d);
+  const int bm = gemm_bm(shape);
+  const int bn_gu = gemm_bn(true, shape), bn_dn = gemm_bn(false, shape);
   const int tk = d.T * d.top_k;
   const bool fp8 = d.w_dtype == MOE_E4M3;
   int32_t* tp_a = at<int32_t>(ws, L.tp_a);
@@ -150,18 +179,18 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   // gate/up with the fused SwiGLU epilogue
   const GemmProblem g0 = problem(a_rows, perm, a_scale, d.D, offsets, tp_a, d.n_local, 0, w_gate, w_up, s_gate, s_up,
                                  static_cast<long long>(d.I) * d.D, h, d.I, d.I, d.D);
-  const int tiles_gu = routed_tile_bound(tk, d.n_local, bm, d.I, kBnSwiglu);
+  const int tiles_gu = routed_tile_bound(tk, d.n_local, bm, d.I, bn_gu);
   GemmProblem gs{};
   if (shared)
     gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr, nullptr, 0, h_sh,
                  d.I_shared, d.I_shared, d.D);
   if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, mf, g0, &gs, tiles_gu, s));
+    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, g0, &gs, tiles_gu, s));
   } else {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, mf, g0, nullptr, tiles_gu, s));
+    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, g0, nullptr, tiles_gu, s));
     if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, hel, true, mf, gs, nullptr,
-                          ((d.T + bm - 1) / bm) * ((d.I_shared + kBnSwiglu - 1) / kBnSwiglu), s));
+      MOE_TRY(launch_gemm(d.act_dtype, hel, true, shape, gs, nullptr,
+                          ((d.T + bm - 1) / bm) * ((d.I_shared + bn_gu - 1) / bn_gu), s));
   }
 
   if (ev_gate_up) MOE_TRY(hipEventRecord(ev_gate_up, s));
@@ -178,19 +207,19 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   }
   const GemmProblem d0 = problem(h_in, nullptr, h_scale, d.I, offsets, tp_b, d.n_local, 0, w_down, nullptr, s_down,
                                  nullptr, static_cast<long long>(d.D) * d.I, out_rows, d.D, d.D, d.I);
-  const int tiles_dn = routed_tile_bound(tk, d.n_local, bm, d.D, kBnPlain);
+  const int tiles_dn = routed_tile_bound(tk, d.n_local, bm, d.D, bn_dn);
   GemmProblem ds{};
   if (shared)
     ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr, nullptr, nullptr, 0,
                  sh_out, d.D, d.D, d.I_shared);
   const int oel = d.out_dtype;
   if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, mf, d0, &ds, tiles_dn, s));
+    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, d0, &ds, tiles_dn, s));
   } else {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, mf, d0, nullptr, tiles_dn, s));
+    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, d0, nullptr, tiles_dn, s));
     if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, oel, false, mf, ds, nullptr,
-                          ((d.T + bm - 1) / bm) * ((d.D + kBnPlain - 1) / kBnPlain), s));
+      MOE_TRY(launch_gemm(d.act_dtype, oel, false, shape, ds, nullptr,
+                          ((d.T + bm - 1) / bm) * ((d.D + bn_dn - 1) / bn_dn), s));
   }
   return MOE_OK;
 }
@@ -205,19 +234,17 @@ size_t moe_workspace_bytes(const moe_dims* dims) {
 }
 
 int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* logits, const float* logit_bias,
-              int32_t* packed, void* stream) {
+              int32_t* packed, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims& d = *dims;
   if (!logits || !packed) return MOE_ERR_NULL_ARG;
   if ((x == nullptr) != (w_router == nullptr)) return MOE_ERR_NULL_ARG;
+  const Layout L = layout(d);
+  if (ws && ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (x) {
-    st = router_logits(d, x, w_router, logits, s);
-    if (st != MOE_OK) return st;
-  }
-  return hip_status(launch_route(logits, logit_bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
+  return route_tokens(d, x, w_router, logits, ws ? at<float>(ws, L.logits_part) : nullptr, logit_bias, packed,
+                      static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, int32_t* offsets, int32_t* perm_token,
@@ -234,8 +261,10 @@ int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, in
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.T == 0) return MOE_OK;
+  const int bm = gemm_bm(expert_shape(d));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), counts, offsets, perm_token, inv_pos, s));
+                         at<int32_t>(ws, L.base), counts, offsets, perm_token, inv_pos, bm, bm,
+                         at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
   if (x) {
     const int tk = d.T * d.top_k;
     if (fp8) {
@@ -305,9 +334,8 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   if (!packed_in) {
     float* logits = logits_out ? logits_out : at<float>(ws, L.logits);
     int32_t* pk = packed_out ? packed_out : at<int32_t>(ws, L.packed);
-    st = router_logits(d, x, w->w_router, logits, s);
+    st = route_tokens(d, x, w->w_router, logits, at<float>(ws, L.logits_part), logit_bias, pk, s);
     if (st != MOE_OK) return st;
-    MOE_TRY(launch_route(logits, logit_bias, d.T, d.E, d.top_k, d.renormalize, pk, s));
     packed = pk;
   } else if (packed_out) {
     MOE_TRY(hipMemcpyAsync(packed_out, packed_in, static_cast<size_t>(d.T) * 2 * d.top_k * 4,
@@ -321,10 +349,10 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm_token);
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
+  const int bm = gemm_bm(expert_shape(d));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), counts, offsets, perm, inv, s));
-  const int bm = gemm_bm(choose_mf(d));
-  MOE_TRY(launch_tile_prefix(offsets, d.n_local, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
+                         at<int32_t>(ws, L.base), counts, offsets, perm, inv, bm, bm, at<int32_t>(ws, L.tp_a),
+                         at<int32_t>(ws, L.tp_b), s));
   const void* a_rows = x;
   const float* a_scale = nullptr;
   if (fp8) {

@@ -16,6 +16,7 @@ template <> struct ElSize<EL_E4M3> { static constexpr int v = 1; };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -51,14 +52,14 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // C[(l / 16) * 4 + r][l % 16], r = 0..3 (row of A, column of B).
 // ---------------------------------------------------------------------------
 
-template <int EL> __device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x4 c);
+template <int EL> __device__ __forceinline__ f32x4 mfma_chunk(const u32x4& a, const u32x4& b, f32x4 c);
 
-template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_BF16>(const uint4& a, const uint4& b, f32x4 c) {
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_BF16>(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
 }
 
-template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_F32>(const uint4& a, const uint4& b, f32x4 c) {
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_F32>(const u32x4& a, const u32x4& b, f32x4 c) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
@@ -66,7 +67,7 @@ template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_F32>(const uint4& a, 
   return c;
 }
 
-template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_E4M3>(const uint4& a, const uint4& b, f32x4 c) {
+template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_E4M3>(const u32x4& a, const u32x4& b, f32x4 c) {
   long a0 = static_cast<long>((static_cast<uint64_t>(a.y) << 32) | a.x);
   long a1 = static_cast<long>((static_cast<uint64_t>(a.w) << 32) | a.z);
   long b0 = static_cast<long>((static_cast<uint64_t>(b.y) << 32) | b.x);

@@ -6,32 +6,40 @@
 // Mixture-of-Experts (MoE)" in "Tối ưu hóa mô hình Qwen 3.5-397B MoE trên hạ tầng TPU
 // Ironwood", whose formula is missing.
 //
-// Work unit (one 256-thread workgroup): one (group, M-tile, N-tile).  The M-tile is
-// 16 or 32 rows of the group (token rows, gathered through perm), the N-tile is
-// 4 waves x NF x 16 output channels (for SwiGLU the same channels of W_gate and
-// W_up, so silu(gate) * up is formed in registers).
+// Work unit (one 256-thread workgroup): one (group, N-tile, M-tile).  The M-tile is up
+// to 16 * MF token rows of the group (gathered through perm); the N-tile is
+// 4 waves x NF x 16 output channels (for SwiGLU the same channels of W_gate and W_up,
+// so silu(gate) * up is formed in registers).
 //
-// Data path, chosen for the weight-streaming regime where each expert has few rows:
-//   * weights go straight from HBM into VGPRs as the MFMA "A" operand: lane l of a
-//     wave reads 16 bytes of output channel (l % 16) at K-byte offset (l / 16) * 16,
-//     so a wave reads 16 rows x 64 contiguous bytes per K step; a K block is 8 steps
-//     (512 bytes of every row), double-buffered in registers (ping-pong), so one
-//     block's loads are in flight while the previous block is multiplied;
-//   * token rows are the MFMA "B" operand, staged per K block in LDS (double
-//     buffered, one barrier per block) because every wave of the workgroup uses them;
-//   * each weight byte is read once per M-tile; M-tiles of one expert are neighbours
-//     in the tile order so repeats hit L2.
-// Tiles are ordered (group, M-tile, N-tile) and dealt to XCDs in contiguous ranges.
+// Data path:
+//   * weights go straight from HBM into VGPRs as the MFMA "A" operand; each wave owns
+//     its own output channels, so weights are never shared between waves and need no
+//     LDS.  Lane l of a wave reads 16 bytes of channel (l % 16) at K-byte offset
+//     (l / 16) * 16, so one wave step covers 16 rows x 64 contiguous bytes; K blocks
+//     of KSTEPS steps rotate through a ring of NBUF register buffers, so the loads of
+//     the next NBUF - 1 blocks are in flight while one block is multiplied;
+//   * token rows are the MFMA "B" operand, shared by the 4 waves: staged per K block in
+//     LDS (double-buffered, one barrier per block), loaded before the weights of the
+//     same block so the LDS store never waits for the weight stream;
+//   * 16-row token fragments past the tile's last row are skipped (uniform branch), so
+//     a ragged group costs MFMA time in 16-row steps only.
+// Two shapes are instantiated: a streaming shape (MF = 1 or 2, two buffers, two
+// workgroups per CU; the down projection takes 4 fragments per wave to double the
+// channels each workgroup streams) for the few-rows-per-expert decode regime, where
+// each weight byte feeds one tile and the kernel is an HBM stream; and a tile shape
+// (MF = 16, 2-step blocks, three buffers, 2 fragments per matrix per wave, one
+// workgroup per CU so a wave may hold 512 registers) for the prefill regime: a 256-row
+// M-tile covers every row of a typical expert (~160 at 8K tokens), so each weight byte
+// is streamed from HBM once and feeds all of the expert's rows, and 32 channels per
+// matrix per wave halve the token bytes staged per MFMA; only experts with more rows
+// (skewed routing) take several M-tiles, adjacent in the launch order.
+// Tiles are ordered (group, N-tile, M-tile) and dealt to XCDs in contiguous ranges.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
-
-constexpr int kKSteps = 8;                // 64-byte K steps per K block
-constexpr int kKBlk = kKSteps * 64;       // bytes of each row per K block
-constexpr int kLdsRow = kKBlk + 16;       // padded LDS row (bytes)
 
 template <int OUT> struct OutStore;
 
@@ -60,20 +68,30 @@ template <> struct OutStore<EL_BF16> {
   }
 };
 
-template <int EL, int OUT, int MF, int NF, bool SWIGLU>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmProblem p0, GemmProblem p1, int has_p1) {
+template <bool NT>
+__device__ __forceinline__ u32x4 load_weight(const uint8_t* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB>
+__global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmProblem p1, int has_p1) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
   constexpr int NMAT = SWIGLU ? 2 : 1;
   constexpr int BN = 4 * NF * 16;
-  constexpr int CPT = BM * (kKBlk / 16) / 256;  // 16-byte A chunks per thread per K block
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kLdsRow];
+  constexpr int KBLK = KSTEPS * 64;   // bytes of each row per K block
+  constexpr int LDS_ROW = KBLK + 16;  // padded LDS row (bytes)
+  constexpr int CHUNKS = BM * (KBLK / 16);
+  static_assert(CHUNKS % 256 == 0, "token tile must split evenly over 256 threads");
+  constexpr int CPT = CHUNKS / 256;   // 16-byte token chunks per thread per K block
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LDS_ROW];
 
   // ---- which tile ---------------------------------------------------------
   const int nt0 = (p0.N + BN - 1) / BN;
   const int nt1 = has_p1 ? (p1.N + BN - 1) / BN : 1;
-  const int tiles0 = (p0.offsets ? p0.tile_prefix[p0.n_groups] : (p0.rows + BM - 1) / BM) * nt0;
-  const int tiles1 = has_p1 ? ((p1.rows + BM - 1) / BM) * nt1 : 0;
+  const int tiles0 = (p0.offsets ? p0.tile_prefix[p0.n_groups] : (p0.rows + BM - 1) / BM * p0.k_splits) * nt0;
+  const int tiles1 = has_p1 ? ((p1.rows + BM - 1) / BM) * p1.k_splits * nt1 : 0;
   const int total = tiles0 + tiles1;
   if (static_cast<int>(blockIdx.x) >= total) return;
   int L = xcd_remap(blockIdx.x, total);
@@ -82,52 +100,64 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmProblem p0, GemmProble
 #define SEL(f) (sec ? p1.f : p0.f)
   const int n_tiles = sec ? nt1 : nt0;
   const int32_t* offsets = SEL(offsets);
-  const int n_tile = L % n_tiles;
-  const int q = L / n_tiles;
-  int g = 0, m = q, row0 = 0, count = SEL(rows);
+  int g = 0, row0 = 0, count = SEL(rows), n_tile, m, ks = 0;
+  const int ksp = SEL(k_splits);
   if (offsets) {
+    // group g owns tiles [pre[g] * n_tiles, pre[g + 1] * n_tiles), ordered (N-tile, M-tile)
     const int32_t* pre = SEL(tile_prefix);
+    const int q = L / n_tiles;
     int lo = 0, hi = SEL(n_groups) - 1;
     while (lo < hi) {  // largest g with pre[g] <= q
       const int mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= q) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    m = q - pre[g];
+    const int mt = pre[g + 1] - pre[g];
+    const int local = L - pre[g] * n_tiles;
+    n_tile = local / mt;
+    m = local % mt;
     row0 = offsets[g];
     count = offsets[g + 1] - row0;
+  } else {
+    const int mt = (count + BM - 1) / BM;
+    m = L % mt;
+    ks = (L / mt) % ksp;
+    n_tile = L / mt / ksp;
   }
   const int rbeg = m * BM;
   const int nrows = min(BM, count - rbeg);
   const int N = SEL(N);
-  const int Kb = SEL(K) * ES;  // bytes per row
-  const uint8_t* A = static_cast<const uint8_t*>(SEL(a));
+  const int Kb_row = SEL(K) * ES;  // bytes per row
+  const int Kb = Kb_row / ksp;     // bytes of this K range
+  const int kofs = ks * Kb;
+  const uint8_t* A = static_cast<const uint8_t*>(SEL(a)) + kofs;
   const int32_t* perm = SEL(perm);
   const size_t lda_b = static_cast<size_t>(SEL(lda)) * ES;
   const size_t wgrp = static_cast<size_t>(g) * SEL(w_stride) * ES;
-  const uint8_t* W0 = static_cast<const uint8_t*>(SEL(w0)) + wgrp;
-  const uint8_t* W1 = SWIGLU ? static_cast<const uint8_t*>(SEL(w1)) + wgrp : nullptr;
+  const uint8_t* W0 = static_cast<const uint8_t*>(SEL(w0)) + wgrp + kofs;
+  const uint8_t* W1 = SWIGLU ? static_cast<const uint8_t*>(SEL(w1)) + wgrp + kofs : nullptr;
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int ncol0 = n_tile * BN + wave * NF * 16;
+  const int mf_active = (nrows + 15) / 16;
 
   // ---- operand pointers ---------------------------------------------------
   const uint8_t* wrow[NMAT][NF];
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
     const int n = min(ncol0 + nf * 16 + lrow, N - 1);
-    wrow[0][nf] = W0 + static_cast<size_t>(n) * Kb + lgrp * 16;
-    if (SWIGLU) wrow[NMAT - 1][nf] = W1 + static_cast<size_t>(n) * Kb + lgrp * 16;
+    wrow[0][nf] = W0 + static_cast<size_t>(n) * Kb_row + lgrp * 16;
+    if (SWIGLU) wrow[NMAT - 1][nf] = W1 + static_cast<size_t>(n) * Kb_row + lgrp * 16;
   }
   const uint8_t* arow[CPT];
   int acol[CPT], aoff[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + i * 256;
-    const int r = c / (kKBlk / 16);
-    acol[i] = (c % (kKBlk / 16)) * 16;
-    aoff[i] = r * kLdsRow + acol[i];
+    const int r = c / (KBLK / 16);
+    acol[i] = (c % (KBLK / 16)) * 16;
+    aoff[i] = r * LDS_ROW + acol[i];
     arow[i] = nullptr;
     if (r < nrows) {
       const int grow = row0 + rbeg + r;
@@ -144,79 +174,94 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmProblem p0, GemmProble
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nblk = (Kb + kKBlk - 1) / kKBlk;
+  // Full K blocks run a branch-free pipeline; a last partial block (K*ES not a
+  // multiple of KBLK, only in small shapes) is handled after it with per-step guards.
+  const int nfull = Kb / KBLK;
+  const int tail_steps = (Kb - nfull * KBLK) / 64;
 
-  auto load_w = [&](uint4 (&w)[NMAT][NF][kKSteps], int kb) {
-    const int off = kb * kKBlk;
-    const int steps = min(kKSteps, (Kb - off) / 64);
+  auto load_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
+    const int off = kb * KBLK;
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s)
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) w[a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * 64);
+  };
+  auto load_a = [&](u32x4 (&av)[CPT], int kb, int bytes) {
+    const int off = kb * KBLK;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      av[i] = u32x4{0u, 0u, 0u, 0u};
+      if (arow[i] && acol[i] < bytes) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + off + acol[i]);
+    }
+  };
+  auto store_a = [&](const u32x4 (&av)[CPT], int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&sA[buf][aoff[i]]) = av[i];
+  };
+  auto step = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int s) {
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      if (MF == 1 || mf < mf_active) {
+        const u32x4 bfr =
+            *reinterpret_cast<const u32x4*>(&sA[buf][(mf * 16 + lrow) * LDS_ROW + s * 64 + lgrp * 16]);
+#pragma unroll
+        for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][s], bfr, acc[a][nf][mf]);
+      }
+    }
+  };
+  auto compute = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) step(w, buf, s);
+  };
+
+  // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
+  // NBUF - 1 blocks before it is multiplied.  Prefetch indices are clamped to the last
+  // block instead of being guarded, so the loop body has no data-dependent branches
+  // (the few repeated loads at the end of a tile hit L2).
+  u32x4 wb[NBUF][NMAT][NF][KSTEPS];
+  u32x4 av[CPT];
+  if (nfull > 0) {
+    load_a(av, 0, KBLK);
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], min(j, nfull - 1));
+    store_a(av, 0);
+    __syncthreads();
+    for (int kb = 0; kb < nfull; kb += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (j > 0 && kb + j >= nfull) break;
+        load_a(av, min(kb + j + 1, nfull - 1), KBLK);
+        load_w(wb[(j + NBUF - 1) % NBUF], min(kb + j + NBUF - 1, nfull - 1));
+        compute(wb[j], (kb + j) & 1);
+        store_a(av, (kb + j + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+  if (tail_steps > 0) {
+    const int buf = nfull & 1;
+    load_a(av, nfull, tail_steps * 64);
+    store_a(av, buf);
+    const int off = nfull * KBLK;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int a = 0; a < NMAT; ++a)
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
-          if (s < steps) w[a][nf][s] = *reinterpret_cast<const uint4*>(wrow[a][nf] + off + s * 64);
-  };
-  auto load_a = [&](uint4 (&av)[CPT], int kb) {
-    const int off = kb * kKBlk;
-    const int bytes = min(kKBlk, Kb - off);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      av[i] = make_uint4(0, 0, 0, 0);
-      if (arow[i] && acol[i] < bytes) av[i] = *reinterpret_cast<const uint4*>(arow[i] + off + acol[i]);
-    }
-  };
-  auto store_a = [&](const uint4 (&av)[CPT], int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(&sA[buf][aoff[i]]) = av[i];
-  };
-  auto compute = [&](const uint4 (&w)[NMAT][NF][kKSteps], int kb) {
-    const int buf = kb & 1;
-    const int steps = min(kKSteps, (Kb - kb * kKBlk) / 64);
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      if (s < steps) {
-        uint4 bfr[MF];
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
-          bfr[mf] = *reinterpret_cast<const uint4*>(&sA[buf][(mf * 16 + lrow) * kLdsRow + s * 64 + lgrp * 16]);
-#pragma unroll
-        for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][s], bfr[mf], acc[a][nf][mf]);
-      }
-    }
-  };
-
-  // ---- main loop: ping-pong register buffers for the weights ---------------
-  uint4 wA[NMAT][NF][kKSteps], wB[NMAT][NF][kKSteps];
-  uint4 av[CPT];
-  load_w(wA, 0);
-  load_a(av, 0);
-  store_a(av, 0);
-  __syncthreads();
-  for (int kb = 0; kb < nblk; kb += 2) {
-    if (kb + 1 < nblk) {
-      load_w(wB, kb + 1);
-      load_a(av, kb + 1);
-    }
-    compute(wA, kb);
-    if (kb + 1 < nblk) store_a(av, (kb + 1) & 1);
+          if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * 64);
     __syncthreads();
-    if (kb + 1 >= nblk) break;
-    if (kb + 2 < nblk) {
-      load_w(wA, kb + 2);
-      load_a(av, kb + 2);
-    }
-    compute(wB, kb + 1);
-    if (kb + 2 < nblk) store_a(av, (kb + 2) & 1);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      if (s < tail_steps) step(wb[0], buf, s);
   }
 
   // ---- epilogue -------------------------------------------------------------
-  void* out = SEL(out);
+  void* out = static_cast<uint8_t*>(SEL(out)) + static_cast<size_t>(ks) * SEL(out_split_stride) * (OUT == EL_F32 ? 4 : 2);
   const size_t ldo = SEL(ldo);
   const float* a_scale = SEL(a_scale);
   const float* s0 = SEL(s0);
@@ -252,47 +297,69 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmProblem p0, GemmProble
 #undef SEL
 }
 
-template <int EL, int OUT, int MF, int NF, bool SWIGLU>
+// Shape of a launch: tile height, K-block depth, weight ring depth, weight load kind,
+// workgroups per CU the register budget is sized for.
+template <int SHAPE, bool SWIGLU> struct Shape;
+template <bool SWIGLU> struct Shape<kShapeStream16, SWIGLU> {
+  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, NBUF = 2, MINB = 2;
+  static constexpr bool NT = false;
+};
+template <bool SWIGLU> struct Shape<kShapeStream32, SWIGLU> {
+  static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2;
+  static constexpr bool NT = false;
+};
+template <bool SWIGLU> struct Shape<kShapeTile256, SWIGLU> {
+  static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1;
+  static constexpr bool NT = false;
+};
+
+template <int EL, int OUT, bool SWIGLU, int SHAPE>
 hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
-  constexpr int BM = 16 * MF, BN = 4 * NF * 16;
+  using S = Shape<SHAPE, SWIGLU>;
+  constexpr int NF = gemm_nf(SWIGLU, SHAPE);
+  constexpr int BM = 16 * S::MF, BN = 4 * NF * 16;
   int tiles1 = 0;
   GemmProblem q1 = p0;
   if (p1) {
     q1 = *p1;
-    tiles1 = ((p1->rows + BM - 1) / BM) * ((p1->N + BN - 1) / BN);
+    tiles1 = ((p1->rows + BM - 1) / BM) * p1->k_splits * ((p1->N + BN - 1) / BN);
   }
   const int grid = max_tiles0 + tiles1;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EL, OUT, MF, NF, SWIGLU>), dim3(grid), dim3(256), 0, stream, p0, q1,
-                     p1 ? 1 : 0);
+  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB>), dim3(grid),
+                     dim3(256), 0, stream, p0, q1, p1 ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int EL, int OUT, bool SWIGLU>
-hipError_t launch_mf(int mf, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
-  constexpr int NF = SWIGLU ? 1 : 2;
-  if (mf == 1) return launch_one<EL, OUT, 1, NF, SWIGLU>(p0, p1, max_tiles0, stream);
-  return launch_one<EL, OUT, 2, NF, SWIGLU>(p0, p1, max_tiles0, stream);
+hipError_t launch_shape(int shape, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
+  switch (shape) {
+    case kShapeStream16: return launch_one<EL, OUT, SWIGLU, kShapeStream16>(p0, p1, max_tiles0, stream);
+    case kShapeStream32: return launch_one<EL, OUT, SWIGLU, kShapeStream32>(p0, p1, max_tiles0, stream);
+    default: return launch_one<EL, OUT, SWIGLU, kShapeTile256>(p0, p1, max_tiles0, stream);
+  }
 }
 
 }  // namespace
 
-int gemm_bm(int mf) { return 16 * mf; }
-
-int gemm_bn(bool swiglu) { return 4 * (swiglu ? 1 : 2) * 16; }
-
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int mf, const GemmProblem& p0, const GemmProblem* p1,
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, const GemmProblem& p0, const GemmProblem* p1,
                        int max_tiles0, hipStream_t stream) {
   if (swiglu) {
-    if (el == EL_F32 && out_el == EL_F32) return launch_mf<EL_F32, EL_F32, true>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_BF16) return launch_mf<EL_BF16, EL_BF16, true>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_BF16) return launch_mf<EL_E4M3, EL_BF16, true>(mf, p0, p1, max_tiles0, stream);
+    if (el == EL_F32 && out_el == EL_F32) return launch_shape<EL_F32, EL_F32, true>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_BF16 && out_el == EL_BF16)
+      return launch_shape<EL_BF16, EL_BF16, true>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_E4M3 && out_el == EL_BF16)
+      return launch_shape<EL_E4M3, EL_BF16, true>(shape, p0, p1, max_tiles0, stream);
   } else {
-    if (el == EL_F32 && out_el == EL_F32) return launch_mf<EL_F32, EL_F32, false>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_BF16) return launch_mf<EL_BF16, EL_BF16, false>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_F32) return launch_mf<EL_BF16, EL_F32, false>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_BF16) return launch_mf<EL_E4M3, EL_BF16, false>(mf, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_F32) return launch_mf<EL_E4M3, EL_F32, false>(mf, p0, p1, max_tiles0, stream);
+    if (el == EL_F32 && out_el == EL_F32) return launch_shape<EL_F32, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_BF16 && out_el == EL_BF16)
+      return launch_shape<EL_BF16, EL_BF16, false>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_BF16 && out_el == EL_F32)
+      return launch_shape<EL_BF16, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_E4M3 && out_el == EL_BF16)
+      return launch_shape<EL_E4M3, EL_BF16, false>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_E4M3 && out_el == EL_F32)
+      return launch_shape<EL_E4M3, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
   }
   return hipErrorInvalidValue;
 }

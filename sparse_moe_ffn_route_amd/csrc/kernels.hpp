@@ -8,6 +8,7 @@ namespace moe {
 
 constexpr int kMaxLocalExperts = 1024;  // LDS histogram rows of the permutation
 constexpr int kPermUnit = 1024;         // (token, slot) pairs per permutation wave
+constexpr int kFusedPermMaxPairs = 16 * 64 * 96;  // up to this many pairs the grouping is one workgroup
 
 inline int perm_units(int T, int k) { return (T * k + kPermUnit - 1) / kPermUnit; }
 
@@ -32,17 +33,35 @@ struct GemmProblem {
   void* out;
   int ldo;                     // elements
   int N, K;
+  int k_splits;                // single-group problems only: K is cut into k_splits equal ranges,
+  long long out_split_stride;  // each writing its partial product at out + split * out_split_stride
 };
 
-// Which tile height a launch uses.
-int gemm_bm(int mf);
+// Launch shapes of the grouped GEMM (see gemm.hip):
+//   stream16 / stream32: 16- or 32-row M-tiles, 8-step K blocks, non-temporal weight
+//                        stream (few rows per expert: decode);
+//   tile256:             256-row M-tiles, 2-step K blocks, one workgroup per CU
+//                        (many rows per expert: prefill).
+enum : int { kShapeStream16 = 0, kShapeStream32 = 1, kShapeTile256 = 2 };
 
-hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k, int renormalize,
-                        int32_t* packed, hipStream_t stream);
+constexpr int gemm_bm(int shape) { return shape == kShapeStream16 ? 16 : shape == kShapeStream32 ? 32 : 256; }
+// 16-column output fragments per wave (per matrix for SwiGLU).
+constexpr int gemm_nf(bool swiglu, int shape) {
+  return shape == kShapeTile256 ? (swiglu ? 2 : 4) : shape == kShapeStream16 ? (swiglu ? 1 : 4) : (swiglu ? 1 : 2);
+}
+// Output channels per workgroup (4 waves).
+constexpr int gemm_bn(bool swiglu, int shape) { return 4 * gemm_nf(swiglu, shape) * 16; }
 
+// Top-k routing.  When n_parts > 1, the logits are the sum of n_parts partial products
+// parts[p][T][E] (added in order p = 0, 1, ...), written to `logits` before routing.
+hipError_t launch_route(const float* parts, int n_parts, float* logits, const float* bias, int T, int E, int k,
+                        int renormalize, int32_t* packed, hipStream_t stream);
+
+// Grouping by expert.  Also writes the M-tile prefixes of both grouped GEMMs (tile heights
+// bm0, bm1) into prefix0 / prefix1 ([n_local + 1]).
 hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
-                          hipStream_t stream);
+                          int bm0, int bm1, int32_t* prefix0, int32_t* prefix1, hipStream_t stream);
 
 hipError_t launch_gather_rows(const void* src, const float* src_scale, const int32_t* perm_token,
                               const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,
@@ -57,9 +76,9 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int
 // Grouped GEMM over up to two problems in one launch (p1 may be NULL).
 //   swiglu: out = silu(A W0^T) * (A W1^T);  else out = A W0^T.
 //   el: operand type (EL_F32 / EL_BF16 / EL_E4M3); out_el: EL_F32 / EL_BF16.
-//   mf: 16-row fragments per tile (1 or 2).
+//   shape: kShapeStream16 / kShapeStream32 / kShapeTile256.
 //   max_tiles0: host upper bound of p0's tiles (its grid share).
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int mf, const GemmProblem& p0, const GemmProblem* p1,
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, const GemmProblem& p0, const GemmProblem* p1,
                        int max_tiles0, hipStream_t stream);
 
 hipError_t launch_combine(int out_el, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,

@@ -124,6 +124,123 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   }
 }
 
+// Whole grouping in one 1024-thread workgroup (used while T*k <= kFusedPermMaxPairs):
+// 16 waves each own one contiguous range of pairs.  Every lane first loads all of its
+// pairs into registers in one batch (one memory latency instead of one per 64 pairs),
+// packed as (token << 11) | (local expert + 1), 0 in the low bits for a non-local
+// expert.  The per-wave histograms, the expert-major scan (with the M-tile prefixes of
+// both GEMMs) and the ballot-ranked scatter then run from registers and LDS, in one
+// launch.
+constexpr int kFusedWaves = 16;
+constexpr int kFusedMaxSteps = kFusedPermMaxPairs / (kFusedWaves * kWave);
+
+__global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
+                                                          int e_begin, int n_local, int n_bits, int bm0, int bm1,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm_token,
+                                                          int32_t* __restrict__ inv_pos, int32_t* __restrict__ prefix0,
+                                                          int32_t* __restrict__ prefix1) {
+  __shared__ int32_t hist[kFusedWaves][kMaxLocalExperts];
+  __shared__ int32_t sc[3][1024];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int per_wave = ((n_pairs + kFusedWaves * kWave - 1) / (kFusedWaves * kWave)) * kWave;
+  const int lo = min(n_pairs, w * per_wave), hi = min(n_pairs, lo + per_wave);
+  const int nsteps = (hi - lo + kWave - 1) / kWave;
+
+  int pv[kFusedMaxSteps];  // -1: past the end; else (t << 11) | (local expert + 1 or 0)
+#pragma unroll
+  for (int s = 0; s < kFusedMaxSteps; ++s) {
+    pv[s] = -1;
+    if (s < nsteps) {
+      const int i = lo + s * kWave + lane;
+      if (i < hi) {
+        const int t = i / k;
+        const int e = packed[static_cast<size_t>(t) * 2 * k + (i - t * k)] - e_begin;
+        pv[s] = (t << 11) | ((e >= 0 && e < n_local) ? e + 1 : 0);
+      }
+    }
+  }
+
+  for (int e = lane; e < n_local; e += kWave) hist[w][e] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int s = 0; s < kFusedMaxSteps; ++s) {
+    if (s < nsteps) {
+      const int e = (pv[s] & 2047) - 1;
+      if (pv[s] >= 0 && e >= 0) atomicAdd(&hist[w][e], 1);
+    }
+  }
+  __syncthreads();
+
+  // expert e = tid: total rows and M-tiles; inclusive scans over experts
+  int tot = 0;
+  if (tid < n_local)
+    for (int v = 0; v < kFusedWaves; ++v) tot += hist[v][tid];
+  const int t0 = (tot + bm0 - 1) / bm0, t1 = (tot + bm1 - 1) / bm1;
+  sc[0][tid] = tot;
+  sc[1][tid] = t0;
+  sc[2][tid] = t1;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int a = 0, b = 0, c = 0;
+    if (tid >= o) {
+      a = sc[0][tid - o];
+      b = sc[1][tid - o];
+      c = sc[2][tid - o];
+    }
+    __syncthreads();
+    sc[0][tid] += a;
+    sc[1][tid] += b;
+    sc[2][tid] += c;
+    __syncthreads();
+  }
+  if (tid < n_local) {
+    const int ex = sc[0][tid] - tot;
+    counts[tid] = tot;
+    offsets[tid] = ex;
+    prefix0[tid + 1] = sc[1][tid];
+    prefix1[tid + 1] = sc[2][tid];
+    int run = ex;  // column tid becomes each wave's first row of expert tid
+    for (int v = 0; v < kFusedWaves; ++v) {
+      const int c = hist[v][tid];
+      hist[v][tid] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[n_local] = sc[0][1023];
+    prefix0[0] = 0;
+    prefix1[0] = 0;
+  }
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int s = 0; s < kFusedMaxSteps; ++s) {
+    if (s < nsteps) {
+      const bool valid = pv[s] >= 0;
+      const int e = valid ? (pv[s] & 2047) - 1 : -1;
+      const bool local = e >= 0;
+      uint64_t same = __ballot(local);
+      for (int b = 0; b < n_bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(local && bit);
+        same &= bit ? m : ~m;
+      }
+      int pos = -1;
+      const int rank = __popcll(same & below);
+      if (local) {
+        pos = hist[w][e] + rank;
+        perm_token[pos] = pv[s] >> 11;
+      }
+      __builtin_amdgcn_wave_barrier();  // every lane has read its base before the leaders advance it
+      if (local && rank == 0) hist[w][e] += __popcll(same);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) inv_pos[lo + s * kWave + lane] = pos;
+    }
+  }
+}
+
 // Row gather: dst[r] = src[perm_token[r]] for r < offsets[n_local]; bytes per row
 // must be a multiple of 16.  One 256-thread block per row.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src,
@@ -240,18 +357,25 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 
 hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
-                          hipStream_t stream) {
+                          int bm0, int bm1, int32_t* prefix0, int32_t* prefix1, hipStream_t stream) {
   const int n_pairs = T * k;
-  const int n_units = perm_units(T, k);
-  const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
   int n_bits = 1;
   while ((1 << n_bits) < n_local) ++n_bits;
+  if (n_pairs <= kFusedPermMaxPairs) {
+    hipLaunchKernelGGL(perm_fused_kernel, dim3(1), dim3(1024), 0, stream, packed, n_pairs, k, e_begin, n_local,
+                       n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1);
+    return hipGetLastError();
+  }
+  const int n_units = perm_units(T, k);
+  const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
                      n_units, hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, base, counts,
                      offsets);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin,
                      n_local, n_bits, n_units, base, perm_token, inv_pos);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, n_local, bm0, bm1, prefix0,
+                     prefix1);
   return hipGetLastError();
 }
 

@@ -26,13 +26,15 @@ __device__ __forceinline__ bool before(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
-                                                    const float* __restrict__ bias, int T, int E, int k,
-                                                    int renormalize, int32_t* __restrict__ packed) {
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ parts, int n_parts,
+                                                    float* __restrict__ logits, const float* __restrict__ bias,
+                                                    int T, int E, int k, int renormalize,
+                                                    int32_t* __restrict__ packed) {
   const int lane = lane_id();
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
-  const float* row = logits + static_cast<size_t>(t) * E;
+  const size_t part_stride = static_cast<size_t>(T) * E;
+  const float* row = (n_parts > 1 ? parts : logits) + static_cast<size_t>(t) * E;
 
   float key[kMaxPerLane];
   uint32_t taken = 0;  // bit i: expert lane + 64 i already selected (or does not exist)
@@ -43,6 +45,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     key[i] = -INFINITY;
     if (i < per_lane && e < E) {
       float v = row[e];
+      if (n_parts > 1) {  // split-K router product: add the partials in a fixed order
+        for (int p = 1; p < n_parts; ++p) v += row[p * part_stride + e];
+        logits[static_cast<size_t>(t) * E + e] = v;
+      }
       if (bias) v = v + bias[e];  // one fp32 add
       key[i] = v;
     } else {
@@ -106,13 +112,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k, int renormalize,
-                        int32_t* packed, hipStream_t stream) {
+hipError_t launch_route(const float* parts, int n_parts, float* logits, const float* bias, int T, int E, int k,
+                        int renormalize, int32_t* packed, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  hipLaunchKernelGGL(route_kernel, grid, dim3(waves_per_block * kWave), 0, stream, logits, bias, T, E, k,
-                     renormalize, packed);
+  hipLaunchKernelGGL(route_kernel, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits, bias, T,
+                     E, k, renormalize, packed);
   return hipGetLastError();
 }
 

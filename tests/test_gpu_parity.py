@@ -146,7 +146,10 @@ def test_route_from_given_logits(T, E, k, kind, renorm):
     np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
 
 
-def test_route_with_router_projection_bf16():
+@pytest.mark.parametrize("split", [False, True])
+def test_route_with_router_projection_bf16(split):
+    """Without scratch the projection is one pass over D; with it, small T splits D into
+    partial products summed in a fixed order by the routing kernel."""
     T, D, E, k = 333, 512, 128, 6
     rng = np.random.default_rng(1)
     x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
@@ -154,7 +157,7 @@ def test_route_with_router_projection_bf16():
     d = moe.make_dims(T, D, E, k, 64)
     logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
     packed = torch.empty(T, 2, k, dtype=torch.int32, device="cuda")
-    moe.moe_route(d, x.cuda(), wr.cuda(), logits, None, packed)
+    moe.moe_route(d, x.cuda(), wr.cuda(), logits, None, packed, ws=moe.workspace(d) if split else None)
     x64, w64 = to_np(x), to_np(wr)
     l_ref = oracle.router_logits(x64, w64).astype(np.float64)
     lg = logits.cpu().numpy()

@@ -71,7 +71,7 @@ def test_bad_dims_rejected(kw):
     assert moe.moe_workspace_bytes(_dims(**kw)) == 0
     lib = moe.library()
     fake = ctypes.c_void_p(256)
-    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None)
+    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None, 0, None)
     assert st == moe.ERR_BAD_DIMS
 
 
@@ -80,7 +80,7 @@ def test_unsupported_rejected(kw):
     assert moe.moe_workspace_bytes(_dims(**kw)) == 0
     lib = moe.library()
     fake = ctypes.c_void_p(256)
-    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None)
+    st = lib.moe_route(ctypes.byref(_dims(**kw)), None, None, fake, None, fake, None, 0, None)
     assert st == moe.ERR_UNSUPPORTED
 
 
@@ -89,10 +89,10 @@ def test_null_arguments_rejected():
     d = _dims()
     fake = ctypes.c_void_p(256)
     assert lib.moe_workspace_bytes(None) == 0
-    assert lib.moe_route(None, None, None, fake, None, fake, None) == moe.ERR_NULL_ARG
-    assert lib.moe_route(ctypes.byref(d), None, None, None, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route(None, None, None, fake, None, fake, None, 0, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, fake, None, 0, None) == moe.ERR_NULL_ARG
     # x without a router weight
-    assert lib.moe_route(ctypes.byref(d), fake, None, fake, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route(ctypes.byref(d), fake, None, fake, None, fake, None, 0, None) == moe.ERR_NULL_ARG
     assert lib.moe_permute(ctypes.byref(d), None, fake, fake, fake, fake, None, None, None, fake, 1 << 20,
                            None) == moe.ERR_NULL_ARG
     assert lib.moe_unpermute_combine(ctypes.byref(d), fake, fake, None, None, fake, None) == moe.ERR_NULL_ARG
@@ -127,7 +127,7 @@ def test_zero_tokens_is_a_no_op():
     w = moe.moe_weights(fake, fake, fake, fake, None, None, None, None, None, None)
     assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, None, None, fake, None, None, fake, need,
                                  None, None) == moe.OK
-    assert lib.moe_route(ctypes.byref(d), None, None, fake, None, fake, None) == moe.OK
+    assert lib.moe_route(ctypes.byref(d), None, None, fake, None, fake, None, 0, None) == moe.OK
 
 
 def test_status_strings():
