@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_bf16")
+    p.add_argument("--layout", default="packed", choices=["packed", "rows"],
+                   help="expert weight layout (packed: repacked once by moe_pack_weights before timing)")
     p.add_argument("--secondary", default="prefill_bf16",
                    help="second workload measured with the same weights ('' to skip)")
     p.add_argument("--secondary-steps", type=int, default=5)
@@ -74,21 +76,23 @@ def committed_traffic(workload):
 class Layer:
     """Buffers and launch of one workload (device inputs shared with another workload when given)."""
 
-    def __init__(self, wl, inp):
+    def __init__(self, wl, inp, packed_w=None):
         import torch
         import sparse_moe_ffn_route_amd as moe
         self.torch, self.moe, self.wl, self.inp = torch, moe, wl, inp
         self.dims = moe.make_dims(wl.T, wl.D, wl.E, wl.top_k, wl.I, wl.I_shared, wl.expert_begin, wl.local,
-                                  wl.renormalize, wl.act, wl.w, wl.out)
+                                  wl.renormalize, wl.act, wl.w, wl.out, "packed" if packed_w else "rows")
+        pw = packed_w or {n: getattr(inp, n) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
         self.ws = moe.workspace(self.dims)
         out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
         self.y = torch.empty(wl.T, wl.D, dtype=out_dt, device="cuda")
         self.logits = None if wl.routing_given else torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
         self.packed = torch.empty(wl.T, 2, wl.top_k, dtype=torch.int32, device="cuda")
         sh = wl.I_shared > 0
-        self.weights = moe.make_weights(inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
-                                        inp.s_down, inp.ws_gate if sh else None, inp.ws_up if sh else None,
-                                        inp.ws_down if sh else None)
+        self.pw = pw
+        self.weights = moe.make_weights(inp.w_router, pw["w_gate"], pw["w_up"], pw["w_down"], inp.s_gate, inp.s_up,
+                                        inp.s_down, pw["ws_gate"] if sh else None, pw["ws_up"] if sh else None,
+                                        pw["ws_down"] if sh else None)
 
     def step(self, events=None):
         self.moe.moe_layer_forward(self.dims, self.weights, self.inp.x, self.inp.packed, self.inp.bias, self.y,
@@ -245,7 +249,13 @@ def main():
     t_gen = time.perf_counter() - t_gen
     print(f"[bench] inputs for {wl.name} drawn on the GPU in {t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    layer = Layer(wl, inp)
+    packed_w = None
+    if args.layout == "packed":
+        import sparse_moe_ffn_route_amd as moe
+        packed_w = {n: (None if getattr(inp, n) is None else moe.moe_pack_weights(getattr(inp, n)))
+                    for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+        torch.cuda.synchronize()
+    layer = Layer(wl, inp, packed_w)
     wall, stages = layer.run(args.steps, args.warmup)
     prim = layer_summary(layer, wall, stages, args.steps)
     print(f"[bench] {wl.name}: {prim['ms_per_step']:.3f} ms/step, stages {stages}", file=sys.stderr, flush=True)
@@ -261,7 +271,7 @@ def main():
             x2 = (torch.randn(wl2.T, wl2.D, generator=g, device="cuda")).to(torch.bfloat16)
             inp2 = synth.LayerInputs(wl2, x2, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
                                      inp.s_down, inp.ws_gate, inp.ws_up, inp.ws_down, None, None)
-            layer2 = Layer(wl2, inp2)
+            layer2 = Layer(wl2, inp2, packed_w)
             wall2, stages2 = layer2.run(args.secondary_steps, 2)
             sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
             sec["roofline"] = roofline_of(layer2, stages2)
@@ -292,7 +302,8 @@ def main():
         "dtype": wl.w if wl.w == "e4m3" else wl.act,
         "data": "synthetic (seeded Philox draws on the GPU; random-init weights)",
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "E": wl.E, "top_k": wl.top_k, "I": wl.I,
-                   "I_shared": wl.I_shared, "expert_slice": [wl.expert_begin, wl.local], "parallelism": "1 GPU"},
+                   "I_shared": wl.I_shared, "expert_slice": [wl.expert_begin, wl.local],
+                   "weight_layout": args.layout, "parallelism": "1 GPU"},
         "roofline": roofline_of(layer, stages),
         "cpu_baseline": cpu,
         "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_roofline_frac", "stage_ms")},

@@ -82,7 +82,14 @@ typedef struct moe_dims {
   int32_t act_dtype;    /* x, router weight, shared weights: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;      /* routed expert weights: MOE_F32 (with act F32), MOE_BF16 or MOE_E4M3 (with act BF16) */
   int32_t out_dtype;    /* y and expert outputs: MOE_F32 or MOE_BF16 */
+  int32_t weight_layout;/* routed and shared expert weights: MOE_LAYOUT_ROWS or MOE_LAYOUT_PACKED */
 } moe_dims;
+
+/* Storage order of the expert weight matrices (router weights are always MOE_LAYOUT_ROWS). */
+enum moe_layout {
+  MOE_LAYOUT_ROWS = 0,   /* row-major [out][in] */
+  MOE_LAYOUT_PACKED = 1  /* fragment-major, as written by moe_pack_weights */
+};
 
 /* Weights of the layer (device pointers). */
 typedef struct moe_weights {
@@ -205,13 +212,36 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const vo
                       int32_t* packed_out, void* ws, size_t ws_bytes, void* const* stage_events,
                       void* stream);
 
+/*
+ * Repack weight matrices from row-major [out][in] into the fragment-major order the
+ * grouped GEMM streams: for each block of 16 output rows ("fragment") and each 64-byte
+ * slice of the reduction dimension, the 16 x 64 bytes are stored as one contiguous
+ * 1 KB run, lane l of the run holding 16 bytes of row (l % 16) at byte (l / 16) * 16 of
+ * the slice.  Every load instruction of the GEMM then reads whole contiguous 1 KB runs
+ * and every fragment is read front to back.  This is a one-time transform at weight
+ * load time; the values are not changed.
+ *
+ *   dtype   MOE_F32, MOE_BF16 or MOE_E4M3 (element size of src / dst)
+ *   n_mats  number of [rows][cols] matrices stored back to back (e.g. n_local experts)
+ *   rows    output rows per matrix (multiple of 16)
+ *   cols    reduction length per row; cols * element size must be a multiple of 64
+ *   src     device, n_mats * rows * cols elements, row-major
+ *   dst     device, same size, must not overlap src
+ * Pack w_gate / w_up as (n_local, I, D), w_down as (n_local, D, I), the shared expert's
+ * gate / up as (1, I_shared, D) and its down as (1, D, I_shared), then set
+ * dims.weight_layout = MOE_LAYOUT_PACKED.  Returns MOE_ERR_BAD_DIMS / MOE_ERR_UNSUPPORTED
+ * for sizes outside these rules, MOE_ERR_NULL_ARG for NULL pointers.
+ */
+int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst,
+                     void* stream);
+
 /* Human-readable text of a moe_status code (static storage). */
 const char* moe_status_string(int status);
 
 /* hipError_t of the last failed launch on the calling host thread (0 if none). */
 int moe_last_hip_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -24,13 +24,17 @@ F32, BF16, E4M3 = 0, 1, 2
 _DTYPE_CODE = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
 _TORCH_OF = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.float8_e4m3fn}
 
+# enum moe_layout
+LAYOUT_ROWS, LAYOUT_PACKED = 0, 1
+_LAYOUT_CODE = {"rows": LAYOUT_ROWS, "packed": LAYOUT_PACKED}
+
 # enum moe_status
 OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine",
-    "moe_layer_forward", "moe_status_string", "moe_last_hip_error", "moe_abi_version",
+    "moe_layer_forward", "moe_pack_weights", "moe_status_string", "moe_last_hip_error", "moe_abi_version",
 )
 
 
@@ -43,7 +47,7 @@ class MoeError(RuntimeError):
 class moe_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "D", "E", "top_k", "I", "I_shared", "expert_begin", "n_local", "renormalize",
-        "act_dtype", "w_dtype", "out_dtype")]
+        "act_dtype", "w_dtype", "out_dtype", "weight_layout")]
 
 
 class moe_weights(ctypes.Structure):
@@ -76,6 +80,8 @@ def library() -> ctypes.CDLL:
     lib.moe_unpermute_combine.restype = i32
     lib.moe_layer_forward.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.moe_layer_forward.restype = i32
+    lib.moe_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.moe_pack_weights.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_hip_error.argtypes = []
@@ -87,9 +93,10 @@ def library() -> ctypes.CDLL:
 
 
 def make_dims(T, D, E, top_k, I, I_shared=0, expert_begin=0, n_local=None, renormalize=True,
-              act="bf16", w="bf16", out="bf16") -> moe_dims:
+              act="bf16", w="bf16", out="bf16", layout="rows") -> moe_dims:
     return moe_dims(T, D, E, top_k, I, I_shared, expert_begin, E if n_local is None else n_local,
-                    1 if renormalize else 0, _DTYPE_CODE[act], _DTYPE_CODE[w], _DTYPE_CODE[out])
+                    1 if renormalize else 0, _DTYPE_CODE[act], _DTYPE_CODE[w], _DTYPE_CODE[out],
+                    _LAYOUT_CODE[layout])
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -180,6 +187,26 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, ev, _stream(stream)),
            "moe_layer_forward")
+
+
+_CODE_OF_TORCH = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3, torch.uint8: E4M3}
+
+
+def moe_pack_weights(src: torch.Tensor, dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Repack [n][rows][cols] (or [rows][cols]) row-major weights into the fragment-major layout."""
+    if src.dim() == 2:
+        n, rows, cols = 1, src.shape[0], src.shape[1]
+    elif src.dim() == 3:
+        n, rows, cols = src.shape
+    else:
+        raise ValueError("weights must be [rows][cols] or [n][rows][cols]")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError("dst must match src in shape and dtype")
+    _check(library().moe_pack_weights(_CODE_OF_TORCH[src.dtype], n, rows, cols, _ptr(src), _ptr(dst),
+                                      _stream(stream)), "moe_pack_weights")
+    return dst
 
 
 def torch_dtype(code: int) -> torch.dtype:

@@ -28,6 +28,7 @@ int check_dims(const moe_dims* d) {
       static_cast<int64_t>(d->expert_begin) + d->n_local > d->E)
     return MOE_ERR_BAD_DIMS;
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_BAD_DIMS;
+  if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_PACKED) return MOE_ERR_BAD_DIMS;
   if (d->top_k > 32 || d->E > 1024 || d->n_local > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
   if (d->D % 64 || d->I % 64 || d->I_shared % 64) return MOE_ERR_UNSUPPORTED;
   const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32 && d->out_dtype == MOE_F32;
@@ -147,7 +148,7 @@ int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* 
     const int shape = router_shape(d);
     const int bm = gemm_bm(shape), bn = gemm_bn(false, shape);
     const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn) * splits;
-    MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, p, nullptr, tiles, s));
+    MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, false, p, nullptr, tiles, s));
     return hip_status(launch_route(parts, splits, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
   }
   return hip_status(launch_route(nullptr, 1, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
@@ -162,6 +163,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                     const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
                     hipStream_t s) {
   const int shape = expert_shape(d);
+  const bool packed = d.weight_layout == MOE_LAYOUT_PACKED;
   const int bm = gemm_bm(shape);
   const int bn_gu = gemm_bn(true, shape), bn_dn = gemm_bn(false, shape);
   const int tk = d.T * d.top_k;
@@ -185,11 +187,11 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
     gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr, nullptr, 0, h_sh,
                  d.I_shared, d.I_shared, d.D);
   if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, g0, &gs, tiles_gu, s));
+    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, packed, g0, &gs, tiles_gu, s));
   } else {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, g0, nullptr, tiles_gu, s));
+    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, packed, g0, nullptr, tiles_gu, s));
     if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, hel, true, shape, gs, nullptr,
+      MOE_TRY(launch_gemm(d.act_dtype, hel, true, shape, packed, gs, nullptr,
                           ((d.T + bm - 1) / bm) * ((d.I_shared + bn_gu - 1) / bn_gu), s));
   }
 
@@ -214,11 +216,11 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                  sh_out, d.D, d.D, d.I_shared);
   const int oel = d.out_dtype;
   if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, d0, &ds, tiles_dn, s));
+    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, packed, d0, &ds, tiles_dn, s));
   } else {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, d0, nullptr, tiles_dn, s));
+    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, packed, d0, nullptr, tiles_dn, s));
     if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, oel, false, shape, ds, nullptr,
+      MOE_TRY(launch_gemm(d.act_dtype, oel, false, shape, packed, ds, nullptr,
                           ((d.T + bm - 1) / bm) * ((d.D + bn_dn - 1) / bn_dn), s));
   }
   return MOE_OK;
@@ -376,6 +378,19 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   return hip_status(mark(5));
 }
 
+int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst,
+                     void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_BAD_DIMS;
+  const int es = dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1;
+  const int64_t row_bytes = static_cast<int64_t>(cols) * es;
+  if (rows % 16 || row_bytes % 64 || row_bytes > (1ll << 30)) return MOE_ERR_UNSUPPORTED;
+  if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_NULL_ARG;
+  return hip_status(launch_pack(src, dst, n_mats, rows, static_cast<int>(row_bytes),
+                                static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
@@ -390,6 +405,6 @@ const char* moe_status_string(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -74,7 +74,7 @@ __device__ __forceinline__ u32x4 load_weight(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB>
+template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED>
 __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmProblem p1, int has_p1) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
@@ -134,8 +134,12 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   const int32_t* perm = SEL(perm);
   const size_t lda_b = static_cast<size_t>(SEL(lda)) * ES;
   const size_t wgrp = static_cast<size_t>(g) * SEL(w_stride) * ES;
-  const uint8_t* W0 = static_cast<const uint8_t*>(SEL(w0)) + wgrp + kofs;
-  const uint8_t* W1 = SWIGLU ? static_cast<const uint8_t*>(SEL(w1)) + wgrp + kofs : nullptr;
+  const uint8_t* W0 = static_cast<const uint8_t*>(SEL(w0)) + wgrp;
+  const uint8_t* W1 = SWIGLU ? static_cast<const uint8_t*>(SEL(w1)) + wgrp : nullptr;
+  // Weight addressing: row-major rows are Kb_row apart and a 64-byte step is 64 bytes on;
+  // in the packed layout a 16-row fragment is one run of 1 KB per step.
+  constexpr int SSTEP = PACKED ? 1024 : 64;     // bytes between consecutive 64-byte K steps
+  constexpr int SBLK = KSTEPS * SSTEP;          // bytes between consecutive K blocks
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -146,9 +150,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   const uint8_t* wrow[NMAT][NF];
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
-    const int n = min(ncol0 + nf * 16 + lrow, N - 1);
-    wrow[0][nf] = W0 + static_cast<size_t>(n) * Kb_row + lgrp * 16;
-    if (SWIGLU) wrow[NMAT - 1][nf] = W1 + static_cast<size_t>(n) * Kb_row + lgrp * 16;
+    size_t off;
+    if (PACKED) {
+      const int frag = min((ncol0 + nf * 16) / 16, N / 16 - 1);
+      off = (static_cast<size_t>(frag) * (Kb_row / 64) + kofs / 64) * 1024 + lane * 16;
+    } else {
+      const int n = min(ncol0 + nf * 16 + lrow, N - 1);
+      off = static_cast<size_t>(n) * Kb_row + kofs + lgrp * 16;
+    }
+    wrow[0][nf] = W0 + off;
+    if (SWIGLU) wrow[NMAT - 1][nf] = W1 + off;
   }
   const uint8_t* arow[CPT];
   int acol[CPT], aoff[CPT];
@@ -179,14 +190,20 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   const int nfull = Kb / KBLK;
   const int tail_steps = (Kb - nfull * KBLK) / 64;
 
+  // Loads of K block kb; past the last block (kb >= nfull) every lane reads the same
+  // 64 bytes at the start of the first token row instead, which stay in L2, so the
+  // ring's tail prefetch costs no memory traffic and the loop needs no branch.
+  const uint8_t* dummy = A + (lane & 3) * 16;
   auto load_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
-    const int off = kb * KBLK;
+    const bool real = kb < nfull;
+    const size_t off = static_cast<size_t>(real ? kb : 0) * SBLK;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int a = 0; a < NMAT; ++a)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) w[a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * 64);
+        for (int nf = 0; nf < NF; ++nf)
+          w[a][nf][s] = load_weight<NTW>(real ? wrow[a][nf] + off + s * SSTEP : dummy);
   };
   auto load_a = [&](u32x4 (&av)[CPT], int kb, int bytes) {
     const int off = kb * KBLK;
@@ -219,15 +236,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   };
 
   // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
-  // NBUF - 1 blocks before it is multiplied.  Prefetch indices are clamped to the last
-  // block instead of being guarded, so the loop body has no data-dependent branches
-  // (the few repeated loads at the end of a tile hit L2).
+  // NBUF - 1 blocks before it is multiplied.  Prefetches past the last block read the
+  // L2-resident dummy instead of being guarded, so the loop body has no data-dependent
+  // branches.
   u32x4 wb[NBUF][NMAT][NF][KSTEPS];
   u32x4 av[CPT];
   if (nfull > 0) {
     load_a(av, 0, KBLK);
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], min(j, nfull - 1));
+    for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], j);
     store_a(av, 0);
     __syncthreads();
     for (int kb = 0; kb < nfull; kb += NBUF) {
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
       for (int j = 0; j < NBUF; ++j) {
         if (j > 0 && kb + j >= nfull) break;
         load_a(av, min(kb + j + 1, nfull - 1), KBLK);
-        load_w(wb[(j + NBUF - 1) % NBUF], min(kb + j + NBUF - 1, nfull - 1));
+        load_w(wb[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
         compute(wb[j], (kb + j) & 1);
         store_a(av, (kb + j + 1) & 1);
         __syncthreads();
@@ -246,14 +263,14 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     const int buf = nfull & 1;
     load_a(av, nfull, tail_steps * 64);
     store_a(av, buf);
-    const int off = nfull * KBLK;
+    const size_t off = static_cast<size_t>(nfull) * SBLK;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int a = 0; a < NMAT; ++a)
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
-          if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * 64);
+          if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * SSTEP);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
@@ -299,23 +316,26 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 
 // Shape of a launch: tile height, K-block depth, weight ring depth, weight load kind,
 // workgroups per CU the register budget is sized for.
-template <int SHAPE, bool SWIGLU> struct Shape;
-template <bool SWIGLU> struct Shape<kShapeStream16, SWIGLU> {
+// NT: non-temporal weight loads, used where each weight byte is read by one tile and
+// the loads cover whole contiguous runs (packed layout); with row-major weights a
+// 128-byte line is split over two load instructions, and the hint costs bandwidth.
+template <int SHAPE, bool SWIGLU, bool PACKED> struct Shape;
+template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream16, SWIGLU, PACKED> {
   static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, NBUF = 2, MINB = 2;
-  static constexpr bool NT = false;
+  static constexpr bool NT = PACKED;
 };
-template <bool SWIGLU> struct Shape<kShapeStream32, SWIGLU> {
+template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream32, SWIGLU, PACKED> {
   static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2;
-  static constexpr bool NT = false;
+  static constexpr bool NT = PACKED;
 };
-template <bool SWIGLU> struct Shape<kShapeTile256, SWIGLU> {
+template <bool SWIGLU, bool PACKED> struct Shape<kShapeTile256, SWIGLU, PACKED> {
   static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1;
   static constexpr bool NT = false;
 };
 
-template <int EL, int OUT, bool SWIGLU, int SHAPE>
+template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
 hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
-  using S = Shape<SHAPE, SWIGLU>;
+  using S = Shape<SHAPE, SWIGLU, PACKED>;
   constexpr int NF = gemm_nf(SWIGLU, SHAPE);
   constexpr int BM = 16 * S::MF, BN = 4 * NF * 16;
   int tiles1 = 0;
@@ -326,41 +346,46 @@ hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tile
   }
   const int grid = max_tiles0 + tiles1;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB>), dim3(grid),
-                     dim3(256), 0, stream, p0, q1, p1 ? 1 : 0);
+  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED>),
+                     dim3(grid), dim3(256), 0, stream, p0, q1, p1 ? 1 : 0);
   return hipGetLastError();
 }
 
-template <int EL, int OUT, bool SWIGLU>
-hipError_t launch_shape(int shape, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
+template <int EL, int OUT, bool SWIGLU, bool PACKED>
+hipError_t launch_layout(int shape, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0,
+                         hipStream_t stream) {
   switch (shape) {
-    case kShapeStream16: return launch_one<EL, OUT, SWIGLU, kShapeStream16>(p0, p1, max_tiles0, stream);
-    case kShapeStream32: return launch_one<EL, OUT, SWIGLU, kShapeStream32>(p0, p1, max_tiles0, stream);
-    default: return launch_one<EL, OUT, SWIGLU, kShapeTile256>(p0, p1, max_tiles0, stream);
+    case kShapeStream16: return launch_one<EL, OUT, SWIGLU, kShapeStream16, PACKED>(p0, p1, max_tiles0, stream);
+    case kShapeStream32: return launch_one<EL, OUT, SWIGLU, kShapeStream32, PACKED>(p0, p1, max_tiles0, stream);
+    default: return launch_one<EL, OUT, SWIGLU, kShapeTile256, PACKED>(p0, p1, max_tiles0, stream);
   }
+}
+
+template <int EL, int OUT, bool SWIGLU>
+hipError_t launch_shape(int shape, bool packed, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0,
+                        hipStream_t stream) {
+  return packed ? launch_layout<EL, OUT, SWIGLU, true>(shape, p0, p1, max_tiles0, stream)
+                : launch_layout<EL, OUT, SWIGLU, false>(shape, p0, p1, max_tiles0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, const GemmProblem& p0, const GemmProblem* p1,
-                       int max_tiles0, hipStream_t stream) {
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p0,
+                       const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
+#define MOE_GEMM(E_, O_, S_) \
+  return launch_shape<E_, O_, S_>(shape, packed, p0, p1, max_tiles0, stream)
   if (swiglu) {
-    if (el == EL_F32 && out_el == EL_F32) return launch_shape<EL_F32, EL_F32, true>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_BF16)
-      return launch_shape<EL_BF16, EL_BF16, true>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_BF16)
-      return launch_shape<EL_E4M3, EL_BF16, true>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_F32 && out_el == EL_F32) MOE_GEMM(EL_F32, EL_F32, true);
+    if (el == EL_BF16 && out_el == EL_BF16) MOE_GEMM(EL_BF16, EL_BF16, true);
+    if (el == EL_E4M3 && out_el == EL_BF16) MOE_GEMM(EL_E4M3, EL_BF16, true);
   } else {
-    if (el == EL_F32 && out_el == EL_F32) return launch_shape<EL_F32, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_BF16)
-      return launch_shape<EL_BF16, EL_BF16, false>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_BF16 && out_el == EL_F32)
-      return launch_shape<EL_BF16, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_BF16)
-      return launch_shape<EL_E4M3, EL_BF16, false>(shape, p0, p1, max_tiles0, stream);
-    if (el == EL_E4M3 && out_el == EL_F32)
-      return launch_shape<EL_E4M3, EL_F32, false>(shape, p0, p1, max_tiles0, stream);
+    if (el == EL_F32 && out_el == EL_F32) MOE_GEMM(EL_F32, EL_F32, false);
+    if (el == EL_BF16 && out_el == EL_BF16) MOE_GEMM(EL_BF16, EL_BF16, false);
+    if (el == EL_BF16 && out_el == EL_F32) MOE_GEMM(EL_BF16, EL_F32, false);
+    if (el == EL_E4M3 && out_el == EL_BF16) MOE_GEMM(EL_E4M3, EL_BF16, false);
+    if (el == EL_E4M3 && out_el == EL_F32) MOE_GEMM(EL_E4M3, EL_F32, false);
   }
+#undef MOE_GEMM
   return hipErrorInvalidValue;
 }
 

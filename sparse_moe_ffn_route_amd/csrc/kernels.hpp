@@ -77,9 +77,13 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int
 //   swiglu: out = silu(A W0^T) * (A W1^T);  else out = A W0^T.
 //   el: operand type (EL_F32 / EL_BF16 / EL_E4M3); out_el: EL_F32 / EL_BF16.
 //   shape: kShapeStream16 / kShapeStream32 / kShapeTile256.
+//   packed: weights in the fragment-major layout of moe_pack_weights (else row-major).
 //   max_tiles0: host upper bound of p0's tiles (its grid share).
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, const GemmProblem& p0, const GemmProblem* p1,
-                       int max_tiles0, hipStream_t stream);
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p0,
+                       const GemmProblem* p1, int max_tiles0, hipStream_t stream);
+
+// Repack n_mats row-major [rows][row_bytes] matrices into the fragment-major layout.
+hipError_t launch_pack(const void* src, void* dst, int64_t n_mats, int rows, int row_bytes, hipStream_t stream);
 
 hipError_t launch_combine(int out_el, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,
                           const void* shared_out, int T, int D, int k, void* y, hipStream_t stream);

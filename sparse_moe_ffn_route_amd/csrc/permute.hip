@@ -132,8 +132,10 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // both GEMMs) and the ballot-ranked scatter then run from registers and LDS, in one
 // launch.
 constexpr int kFusedWaves = 16;
-constexpr int kFusedMaxSteps = kFusedPermMaxPairs / (kFusedWaves * kWave);
 
+// MAXSTEPS: compile-time bound on the 64-pair steps of one wave (the register array of
+// preloaded pairs); a small instance keeps the decode-sized launch's code short.
+template <int MAXSTEPS>
 __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
                                                           int e_begin, int n_local, int n_bits, int bm0, int bm1,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -147,9 +149,9 @@ __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restr
   const int lo = min(n_pairs, w * per_wave), hi = min(n_pairs, lo + per_wave);
   const int nsteps = (hi - lo + kWave - 1) / kWave;
 
-  int pv[kFusedMaxSteps];  // -1: past the end; else (t << 11) | (local expert + 1 or 0)
+  int pv[MAXSTEPS];  // -1: past the end; else (t << 11) | (local expert + 1 or 0)
 #pragma unroll
-  for (int s = 0; s < kFusedMaxSteps; ++s) {
+  for (int s = 0; s < MAXSTEPS; ++s) {
     pv[s] = -1;
     if (s < nsteps) {
       const int i = lo + s * kWave + lane;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restr
   for (int e = lane; e < n_local; e += kWave) hist[w][e] = 0;
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int s = 0; s < kFusedMaxSteps; ++s) {
+  for (int s = 0; s < MAXSTEPS; ++s) {
     if (s < nsteps) {
       const int e = (pv[s] & 2047) - 1;
       if (pv[s] >= 0 && e >= 0) atomicAdd(&hist[w][e], 1);
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restr
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int s = 0; s < kFusedMaxSteps; ++s) {
+  for (int s = 0; s < MAXSTEPS; ++s) {
     if (s < nsteps) {
       const bool valid = pv[s] >= 0;
       const int e = valid ? (pv[s] & 2047) - 1 : -1;
@@ -361,9 +363,15 @@ hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int 
   const int n_pairs = T * k;
   int n_bits = 1;
   while ((1 << n_bits) < n_local) ++n_bits;
-  if (n_pairs <= kFusedPermMaxPairs) {
-    hipLaunchKernelGGL(perm_fused_kernel, dim3(1), dim3(1024), 0, stream, packed, n_pairs, k, e_begin, n_local,
+  if (n_pairs <= kFusedWaves * kWave * 8) {
+    hipLaunchKernelGGL(perm_fused_kernel<8>, dim3(1), dim3(1024), 0, stream, packed, n_pairs, k, e_begin, n_local,
                        n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1);
+    return hipGetLastError();
+  }
+  if (n_pairs <= kFusedPermMaxPairs) {
+    hipLaunchKernelGGL(perm_fused_kernel<kFusedPermMaxPairs / (kFusedWaves * kWave)>, dim3(1), dim3(1024), 0,
+                       stream, packed, n_pairs, k, e_begin, n_local, n_bits, bm0, bm1, counts, offsets, perm_token,
+                       inv_pos, prefix0, prefix1);
     return hipGetLastError();
   }
   const int n_units = perm_units(T, k);

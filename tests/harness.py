@@ -16,33 +16,44 @@ import synth
 _OUT_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def dims_of(wl: synth.Workload, shared: bool = True) -> moe.moe_dims:
+def dims_of(wl: synth.Workload, shared: bool = True, packed: bool = False) -> moe.moe_dims:
     return moe.make_dims(wl.T, wl.D, wl.E, wl.top_k, wl.I, wl.I_shared if shared else 0, wl.expert_begin,
-                         wl.local, wl.renormalize, wl.act, wl.w, wl.out)
+                         wl.local, wl.renormalize, wl.act, wl.w, wl.out, "packed" if packed else "rows")
+
+
+def packed_weights(dev: synth.LayerInputs) -> dict:
+    """Expert and shared weights repacked on the GPU by moe_pack_weights."""
+    out = {}
+    for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        t = getattr(dev, name)
+        out[name] = None if t is None else moe.moe_pack_weights(t)
+    return out
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def gpu_layer(inp: synth.LayerInputs, shared: bool = True, ws: torch.Tensor = None) -> dict:
+def gpu_layer(inp: synth.LayerInputs, shared: bool = True, ws: torch.Tensor = None, packed: bool = False) -> dict:
     """moe_layer_forward on the inputs (moved to the GPU); returns host copies."""
     wl = inp.wl
     dev = inp if inp.x.is_cuda else inp.to("cuda")
-    d = dims_of(wl, shared)
+    d = dims_of(wl, shared, packed)
     y = torch.empty(wl.T, wl.D, dtype=_OUT_TORCH[wl.out], device="cuda")
     logits = None if wl.routing_given else torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
-    packed = torch.empty(wl.T, 2, wl.top_k, dtype=torch.int32, device="cuda")
+    blob = torch.empty(wl.T, 2, wl.top_k, dtype=torch.int32, device="cuda")
     if ws is None:
         ws = moe.workspace(d)
     use_shared = shared and wl.I_shared > 0
-    w = moe.make_weights(dev.w_router, dev.w_gate, dev.w_up, dev.w_down, dev.s_gate, dev.s_up, dev.s_down,
-                         dev.ws_gate if use_shared else None, dev.ws_up if use_shared else None,
-                         dev.ws_down if use_shared else None)
-    moe.moe_layer_forward(d, w, dev.x, dev.packed, dev.bias, y, logits, packed, ws)
+    pw = packed_weights(dev) if packed else {n: getattr(dev, n) for n in
+                                             ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    w = moe.make_weights(dev.w_router, pw["w_gate"], pw["w_up"], pw["w_down"], dev.s_gate, dev.s_up, dev.s_down,
+                         pw["ws_gate"] if use_shared else None, pw["ws_up"] if use_shared else None,
+                         pw["ws_down"] if use_shared else None)
+    moe.moe_layer_forward(d, w, dev.x, dev.packed, dev.bias, y, logits, blob, ws)
     torch.cuda.synchronize()
     return dict(y=to_np(y), logits=None if logits is None else logits.cpu().numpy(),
-                packed=packed.cpu().numpy(), dev=dev)
+                packed=blob.cpu().numpy(), dev=dev)
 
 
 def oracle_routing(inp: synth.LayerInputs, logits=None):

@@ -63,9 +63,9 @@ def _check_grouping(inp, packed_np):
     return c
 
 
-def _check_routed_layer(inp, seed):
+def _check_routed_layer(inp, seed, packed=True):
     wl = inp.wl
-    g = gpu_layer(inp)
+    g = gpu_layer(inp, packed=packed)
     # routing of every token, from the GPU's fp32 logits
     bias = None if inp.bias is None else inp.bias.cpu().numpy()
     ids, w = oracle.route(g["logits"], wl.top_k, bias=bias, renormalize=wl.renormalize)
@@ -81,8 +81,8 @@ def _check_routed_layer(inp, seed):
     ref = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp), shared=synth.shared_f64(inp))
     err = rel_err(g["y"][s], ref["y"])
     assert err <= tolerance(wl), f"{wl.name}: sampled rel err {err:.3e}"
-    # the routed part alone (shared expert off) on the same tokens
-    g2 = gpu_layer(inp, shared=False)
+    # the routed part alone (shared expert off) on the same tokens, row-major weights
+    g2 = gpu_layer(inp, shared=False, packed=False)
     ref2 = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp), shared=None)
     err2 = rel_err(g2["y"][s], ref2["y"])
     assert err2 <= tolerance(wl), f"{wl.name} (no shared): sampled rel err {err2:.3e}"
@@ -108,7 +108,7 @@ def test_skewed_prefill_full_size(big_layer):
 def test_ep_share_fp8_full_size():
     wl = synth.WORKLOADS["ep_share_fp8"]
     inp = synth.make_inputs(wl, 0, "cuda")
-    g = gpu_layer(inp)
+    g = gpu_layer(inp, packed=True)
     np.testing.assert_array_equal(g["packed"], inp.packed.cpu().numpy())   # the given blob passes through
     counts = _check_grouping(inp, g["packed"])
     assert 9000 < counts.sum() < 11500                    # ~T*k*64/512 pairs are local

@@ -54,9 +54,9 @@ MID = {
 }
 
 
-def _check_layer(wl, seed=0, shared=True):
+def _check_layer(wl, seed=0, shared=True, packed=False):
     inp = synth.make_inputs(wl, seed, "cpu")
-    g = gpu_layer(inp, shared=shared)
+    g = gpu_layer(inp, shared=shared, packed=packed)
     if not wl.routing_given:
         x64, wr64 = synth.f64(inp.x), synth.f64(inp.w_router)
         l_ref = oracle.router_logits(x64, wr64).astype(np.float64)
@@ -75,6 +75,25 @@ def _check_layer(wl, seed=0, shared=True):
 @pytest.mark.parametrize("name", list(MID))
 def test_layer_forward_parity(name):
     _check_layer(MID[name])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mid_fp32", "decode_like_bf16", "mid_bf16", "mid_bf16_f32out",
+                                  "skew_bf16", "slice_fp8", "slice_fp8_f32out", "one_token"])
+def test_layer_forward_parity_packed_weights(name):
+    """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
+    _check_layer(MID[name], seed=2, packed=True)
+
+
+def test_pack_weights_layout():
+    """moe_pack_weights places row (16 f + l % 16), bytes [64 s + 16 (l / 16), +16) at run (f, s), chunk l."""
+    rng = np.random.default_rng(3)
+    n, rows, cols = 3, 48, 256
+    src = torch.from_numpy(rng.integers(0, 2 ** 16, (n, rows, cols), dtype=np.int64).astype(np.int16))
+    src = src.view(torch.bfloat16).cuda()
+    dst = moe.moe_pack_weights(src).cpu().view(torch.int16).numpy()
+    a = src.cpu().view(torch.int16).numpy().reshape(n, rows // 16, 16, cols * 2 // 64, 4, 8)  # [n][f][r][s][g][8 elems]
+    expect = a.transpose(0, 1, 3, 4, 2, 5).reshape(-1)                                        # [n][f][s][g][r][8]
+    np.testing.assert_array_equal(dst.reshape(-1), expect)
 
 
 @pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "tiny_fp32", "skew_bf16"])
@@ -180,6 +199,7 @@ PERM_CASES = [
     (1, 1, 4, 0, 4, False),
     (2049, 8, 1024, 0, 1024, False),
     (777, 3, 16, 5, 1, True),
+    (12000, 10, 512, 128, 64, True),   # beyond the one-workgroup path: histogram / scan / scatter kernels
 ]
 
 

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(moe.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_library_targets_gfx950_only():
@@ -61,6 +61,17 @@ def _dims(**kw):
 
 BAD_DIMS = [dict(T=-1), dict(D=0), dict(E=0), dict(top_k=0), dict(top_k=9), dict(I=0), dict(I_shared=-64),
             dict(expert_begin=6, n_local=4), dict(expert_begin=-1, n_local=2)]
+
+
+def test_pack_weights_argument_checks():
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_pack_weights(3, 1, 16, 64, fake, fake, None) == moe.ERR_UNSUPPORTED      # dtype
+    assert lib.moe_pack_weights(moe.BF16, 1, 24, 64, fake, fake, None) == moe.ERR_UNSUPPORTED  # rows % 16
+    assert lib.moe_pack_weights(moe.BF16, 1, 16, 48, fake, fake, None) == moe.ERR_UNSUPPORTED  # 96 B rows
+    assert lib.moe_pack_weights(moe.BF16, -1, 16, 64, fake, fake, None) == moe.ERR_BAD_DIMS
+    assert lib.moe_pack_weights(moe.BF16, 1, 16, 64, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_pack_weights(moe.BF16, 0, 16, 64, None, None, None) == moe.OK              # nothing to do
 UNSUPPORTED = [dict(D=96), dict(I=100), dict(I_shared=32), dict(E=2048, top_k=2), dict(E=64, top_k=33),
                dict(act="f32", w="bf16"), dict(act="f32", w="f32", out="bf16"), dict(act="bf16", w="f32"),
                dict(act="e4m3", w="e4m3")]
