@@ -59,7 +59,7 @@ int router_splits(const moe_dims& d) {
 }
 
 struct Layout {
-  size_t logits, logits_part, packed, hist, base, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
+  size_t logits, logits_part, packed, hist, base, rank, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
   size_t xq, sx, h, h_sh, hq, sh, out_rows, sh_out, total;
 };
 
@@ -81,6 +81,7 @@ Layout layout(const moe_dims& d) {
   L.packed = take(tk * 2 * 4);
   L.hist = take(nl * U * 4);
   L.base = take(nl * U * 4);
+  L.rank = take(tk * 4);
   L.counts = take(nl * 4);
   L.offsets = take((nl + 1) * 4);
   L.tp_a = take((nl + 1) * 4);
@@ -265,7 +266,7 @@ int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, in
   if (d.T == 0) return MOE_OK;
   const int bm = gemm_bm(expert_shape(d));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), counts, offsets, perm_token, inv_pos, bm, bm,
+                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm_token, inv_pos, bm, bm,
                          at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
   if (x) {
     const int tk = d.T * d.top_k;
@@ -353,7 +354,8 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
   const int bm = gemm_bm(expert_shape(d));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), counts, offsets, perm, inv, bm, bm, at<int32_t>(ws, L.tp_a),
+                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm, inv, bm, bm,
+                         at<int32_t>(ws, L.tp_a),
                          at<int32_t>(ws, L.tp_b), s));
   const void* a_rows = x;
   const float* a_scale = nullptr;

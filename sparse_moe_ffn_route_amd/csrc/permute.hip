@@ -7,16 +7,14 @@
 // expert parallelism only the device's own expert slice is grouped (section
 // "Fusing Three Collectives Into Two").
 //
-// Deterministic without atomics deciding positions:
-//   1. histogram: the token-major list of T*k pairs is cut into units of 1024 pairs,
-//      one wave per unit, counted in a per-wave LDS histogram -> hist[e][unit];
-//   2. scan: one workgroup scans hist in expert-major order -> base[e][unit],
-//      offsets, counts;
-//   3. scatter: each wave re-walks its unit 64 pairs at a time; lanes holding the
-//      same expert find each other with one ballot per bit of the expert id, rank
-//      themselves by lane order, and the lowest lane advances that expert's running
-//      count.  Row = base[e][unit] + running + rank, i.e. (t, j) order within each
-//      expert.
+// Deterministic without atomics deciding positions: lanes holding the same expert find
+// each other with one ballot per bit of the expert id and rank themselves by lane
+// order; the lowest lane advances that expert's running count.  The row of a pair is
+// (rows of lower experts) + (earlier pairs of the same expert), i.e. experts ascending
+// and (t, j) ascending inside an expert.
+//   * up to 8192 pairs (decode sizes): one 1024-thread workgroup does everything;
+//   * beyond: rank within 1024-pair units (one wave each), one-workgroup scan over
+//     experts, then one thread per pair places it.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,105 +24,129 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ int pair_expert(const int32_t* packed, int i, int k) {
-  const int t = i / k, j = i - t * k;
-  return packed[static_cast<size_t>(t) * 2 * k + j];
+constexpr int kUnitSteps = kPermUnit / kWave;  // 64-pair steps of one unit (16)
+
+// Local expert of pair i of the token-major list, -1 if the expert is not local.
+__device__ __forceinline__ int local_expert(const int32_t* packed, int i, int k, int e_begin, int n_local) {
+  const int t = i / k;
+  const int e = packed[static_cast<size_t>(t) * 2 * k + (i - t * k)] - e_begin;
+  return (e >= 0 && e < n_local) ? e : -1;
 }
 
-__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
-                                                        int e_begin, int n_local, int n_units,
-                                                        int32_t* __restrict__ hist) {
-  __shared__ int32_t h[kWavesPerBlock][kMaxLocalExperts];
-  const int w = threadIdx.x / kWave, lane = lane_id();
-  const int u = blockIdx.x * kWavesPerBlock + w;
-  if (u >= n_units) return;  // whole wave leaves together; waves use disjoint LDS rows
-  for (int e = lane; e < n_local; e += kWave) h[w][e] = 0;
-  __builtin_amdgcn_wave_barrier();
-  const int end = min(n_pairs, (u + 1) * kPermUnit);
-  for (int i = u * kPermUnit + lane; i < end; i += kWave) {
-    const int e = pair_expert(packed, i, k) - e_begin;
-    if (e >= 0 && e < n_local) atomicAdd(&h[w][e], 1);
-  }
-  __builtin_amdgcn_wave_barrier();
-  for (int e = lane; e < n_local; e += kWave) hist[static_cast<size_t>(e) * n_units + u] = h[w][e];
-}
-
-// One workgroup of 1024 threads: exclusive scan of hist (expert-major) into base.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int n_local,
-                                                         int n_units, int32_t* __restrict__ base,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets) {
-  __shared__ int32_t part[1024];
-  const int n = n_local * n_units;
-  const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += hist[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;  // exclusive prefix of this thread's chunk
-  for (int i = lo; i < hi; ++i) {
-    const int c = hist[i];
-    base[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  const int total = part[1023];
-  for (int e = tid; e < n_local; e += 1024) {
-    const int b0 = base[static_cast<size_t>(e) * n_units];
-    const int b1 = (e + 1 < n_local) ? base[static_cast<size_t>(e + 1) * n_units] : total;
-    offsets[e] = b0;
-    counts[e] = b1 - b0;
-  }
-  if (tid == 0) offsets[n_local] = total;
-}
-
-__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ packed, int n_pairs,
-                                                           int k, int e_begin, int n_local, int n_bits,
-                                                           int n_units, const int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ perm_token,
-                                                           int32_t* __restrict__ inv_pos) {
+// Stage 1 of the multi-workgroup grouping: one wave per unit of kPermUnit consecutive
+// pairs.  The wave loads all its pairs first (one memory latency), then walks them 64
+// at a time: lanes holding the same expert find each other with one ballot per id bit,
+// rank themselves by lane order, and the lowest lane advances that expert's running
+// count in LDS.  Output: each local pair's rank inside its unit, and hist[unit][e].
+__global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
+                                                        int e_begin, int n_local, int n_bits, int n_units,
+                                                        int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __shared__ int32_t run[kWavesPerBlock][kMaxLocalExperts];
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int u = blockIdx.x * kWavesPerBlock + w;
-  if (u >= n_units) return;
+  if (u >= n_units) return;  // whole wave leaves together; waves use disjoint LDS rows
+  const int base_i = u * kPermUnit;
+  int pe[kUnitSteps];
+#pragma unroll
+  for (int s = 0; s < kUnitSteps; ++s) {
+    const int i = base_i + s * kWave + lane;
+    pe[s] = i < n_pairs ? local_expert(packed, i, k, e_begin, n_local) : -1;
+  }
   for (int e = lane; e < n_local; e += kWave) run[w][e] = 0;
   __builtin_amdgcn_wave_barrier();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int end = min(n_pairs, (u + 1) * kPermUnit);
-  for (int i0 = u * kPermUnit; i0 < end; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool valid = i < end;
-    const int e = valid ? pair_expert(packed, i, k) - e_begin : -1;
-    const bool local = valid && e >= 0 && e < n_local;
+#pragma unroll
+  for (int s = 0; s < kUnitSteps; ++s) {
+    const int e = pe[s];
+    const bool local = e >= 0;
     uint64_t same = __ballot(local);
     for (int b = 0; b < n_bits; ++b) {
       const bool bit = (e >> b) & 1;
       const uint64_t m = __ballot(local && bit);
       same &= bit ? m : ~m;
     }
-    int pos = -1;
-    if (local) {
-      const int rank = __popcll(same & below);
-      pos = base[static_cast<size_t>(e) * n_units + u] + run[w][e] + rank;
-      perm_token[pos] = i / k;
-    }
-    __builtin_amdgcn_wave_barrier();  // every lane has read run[] before the leaders advance it
-    if (local && __popcll(same & below) == 0) run[w][e] += __popcll(same);
+    const int r = __popcll(same & below);
+    if (local) rank[base_i + s * kWave + lane] = run[w][e] + r;
+    __builtin_amdgcn_wave_barrier();  // every lane has read its count before the leaders advance it
+    if (local && r == 0) run[w][e] += __popcll(same);
     __builtin_amdgcn_wave_barrier();
-    if (valid) inv_pos[i] = pos;
+  }
+  for (int e = lane; e < n_local; e += kWave) hist[static_cast<size_t>(u) * n_local + e] = run[w][e];
+}
+
+// Stage 2: one workgroup, thread e owns expert e (n_local <= 1024).  Expert totals and
+// M-tile counts are scanned over experts; hist[unit][e] becomes base[unit][e], the first
+// grouped row of expert e coming from that unit.  Each pass over units reads one
+// contiguous row of n_local counts across the workgroup.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int n_local,
+                                                         int n_units, int bm0, int bm1, int32_t* __restrict__ base,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ prefix0,
+                                                         int32_t* __restrict__ prefix1) {
+  __shared__ int32_t sc[3][1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < n_local) {
+#pragma unroll 8
+    for (int u = 0; u < n_units; ++u) tot += hist[static_cast<size_t>(u) * n_local + e];
+  }
+  sc[0][e] = tot;
+  sc[1][e] = (tot + bm0 - 1) / bm0;
+  sc[2][e] = (tot + bm1 - 1) / bm1;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int a = 0, b = 0, c = 0;
+    if (e >= o) {
+      a = sc[0][e - o];
+      b = sc[1][e - o];
+      c = sc[2][e - o];
+    }
+    __syncthreads();
+    sc[0][e] += a;
+    sc[1][e] += b;
+    sc[2][e] += c;
+    __syncthreads();
+  }
+  if (e < n_local) {
+    int run = sc[0][e] - tot;
+    counts[e] = tot;
+    offsets[e] = run;
+    prefix0[e + 1] = sc[1][e];
+    prefix1[e + 1] = sc[2][e];
+#pragma unroll 8
+    for (int u = 0; u < n_units; ++u) {
+      const size_t at = static_cast<size_t>(u) * n_local + e;
+      const int c = hist[at];
+      base[at] = run;
+      run += c;
+    }
+  }
+  if (e == 0) {
+    offsets[n_local] = sc[0][1023];
+    prefix0[0] = 0;
+    prefix1[0] = 0;
   }
 }
 
-// Whole grouping in one 1024-thread workgroup (used while T*k <= kFusedPermMaxPairs):
+// Stage 3: one thread per pair: row = base[e][unit] + rank inside the unit.
+__global__ __launch_bounds__(256) void perm_place_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
+                                                         int e_begin, int n_local, int n_units,
+                                                         const int32_t* __restrict__ base,
+                                                         const int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ perm_token,
+                                                         int32_t* __restrict__ inv_pos) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_pairs) return;
+  const int e = local_expert(packed, i, k, e_begin, n_local);
+  int pos = -1;
+  if (e >= 0) {
+    pos = base[static_cast<size_t>(i / kPermUnit) * n_local + e] + rank[i];
+    perm_token[pos] = i / k;
+  }
+  inv_pos[i] = pos;
+}
+
+// Whole grouping in one 1024-thread workgroup (used up to 16 * 64 * 8 pairs):
 // 16 waves each own one contiguous range of pairs.  Every lane first loads all of its
 // pairs into registers in one batch (one memory latency instead of one per 64 pairs),
 // packed as (token << 11) | (local expert + 1), 0 in the low bits for a non-local
@@ -358,8 +380,9 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 }  // namespace
 
 hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
-                          int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
-                          int bm0, int bm1, int32_t* prefix0, int32_t* prefix1, hipStream_t stream) {
+                          int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                          int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0, int32_t* prefix1,
+                          hipStream_t stream) {
   const int n_pairs = T * k;
   int n_bits = 1;
   while ((1 << n_bits) < n_local) ++n_bits;
@@ -368,22 +391,14 @@ hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int 
                        n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1);
     return hipGetLastError();
   }
-  if (n_pairs <= kFusedPermMaxPairs) {
-    hipLaunchKernelGGL(perm_fused_kernel<kFusedPermMaxPairs / (kFusedWaves * kWave)>, dim3(1), dim3(1024), 0,
-                       stream, packed, n_pairs, k, e_begin, n_local, n_bits, bm0, bm1, counts, offsets, perm_token,
-                       inv_pos, prefix0, prefix1);
-    return hipGetLastError();
-  }
   const int n_units = perm_units(T, k);
   const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
-                     n_units, hist);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, base, counts,
-                     offsets);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin,
-                     n_local, n_bits, n_units, base, perm_token, inv_pos);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, n_local, bm0, bm1, prefix0,
-                     prefix1);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
+                     n_bits, n_units, rank, hist);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, bm0, bm1, base,
+                     counts, offsets, prefix0, prefix1);
+  hipLaunchKernelGGL(perm_place_kernel, dim3((n_pairs + 255) / 256), dim3(256), 0, stream, packed, n_pairs, k,
+                     e_begin, n_local, n_units, base, rank, perm_token, inv_pos);
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ __device__ __forceinline__ bool before(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// SPLIT: the router product arrives as n_parts > 1 partial sums over slices of D.
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ parts, int n_parts,
                                                     float* __restrict__ logits, const float* __restrict__ bias,
                                                     int T, int E, int k, int renormalize,
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ pa
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   const size_t part_stride = static_cast<size_t>(T) * E;
-  const float* row = (n_parts > 1 ? parts : logits) + static_cast<size_t>(t) * E;
+  const float* row = (SPLIT ? parts : logits) + static_cast<size_t>(t) * E;
 
   float key[kMaxPerLane];
   uint32_t taken = 0;  // bit i: expert lane + 64 i already selected (or does not exist)
@@ -45,14 +47,34 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ pa
     key[i] = -INFINITY;
     if (i < per_lane && e < E) {
       float v = row[e];
-      if (n_parts > 1) {  // split-K router product: add the partials in a fixed order
-        for (int p = 1; p < n_parts; ++p) v += row[p * part_stride + e];
-        logits[static_cast<size_t>(t) * E + e] = v;
-      }
-      if (bias) v = v + bias[e];  // one fp32 add
+      if (!SPLIT && bias) v = v + bias[e];  // one fp32 add
       key[i] = v;
     } else {
       taken |= 1u << i;
+    }
+  }
+  if (SPLIT) {
+    // add the partials in a fixed order; each partial's loads are issued together, so
+    // the sum costs one memory latency per partial
+#pragma unroll 1
+    for (int p = 1; p < n_parts; ++p) {
+      const float* prow = row + p * part_stride;
+      float v[kMaxPerLane];
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + i * kWave;
+        v[i] = (i < per_lane && e < E) ? prow[e] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) key[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + i * kWave;
+      if (i < per_lane && e < E) {
+        logits[static_cast<size_t>(t) * E + e] = key[i];
+        if (bias) key[i] = key[i] + bias[e];  // one fp32 add
+      }
     }
   }
 
@@ -117,8 +139,12 @@ hipError_t launch_route(const float* parts, int n_parts, float* logits, const fl
   if (T == 0) return hipSuccess;
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  hipLaunchKernelGGL(route_kernel, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits, bias, T,
-                     E, k, renormalize, packed);
+  if (n_parts > 1)
+    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits,
+                       bias, T, E, k, renormalize, packed);
+  else
+    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits,
+                       bias, T, E, k, renormalize, packed);
   return hipGetLastError();
 }
 
