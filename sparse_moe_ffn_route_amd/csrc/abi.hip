@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -114,10 +116,21 @@ int hip_status(hipError_t e) {
     if (_s != MOE_OK) return _s;             \
   } while (0)
 
-// Shape of the grouped expert GEMMs: the average routed rows per expert decides.
-int expert_shape(const moe_dims& d) {
+// Shape of the grouped expert GEMMs: the average routed rows per expert decides.  The
+// tile shape addresses its operands with 32-bit offsets; batches whose operands do not
+// fit below 2 GiB take the 32-row streaming shape instead.  gathered: the gate/up A
+// operand is x ([T][D], read through perm) rather than grouped rows ([T * top_k][D]).
+int expert_shape(const moe_dims& d, bool gathered) {
   const double avg = static_cast<double>(d.T) * d.top_k / d.E;
-  return avg <= 16.0 ? kShapeStream16 : avg <= 32.0 ? kShapeStream32 : kShapeTile256;
+  if (avg <= 16.0) return kShapeStream16;
+  if (avg <= 32.0) return kShapeStream32;
+  const int64_t lim = 1ll << 31, tk = static_cast<int64_t>(d.T) * d.top_k;
+  const int64_t ea = act_size(d.act_dtype);
+  const int64_t ih = std::max(d.I, d.I_shared);
+  const bool fits = (gathered ? d.T : tk) * d.D * ea < lim && tk * d.I * 4 < lim &&
+                    static_cast<int64_t>(d.T) * d.I_shared * 4 < lim && static_cast<int64_t>(d.T) * d.D * ea < lim &&
+                    ih * d.D * 4 < lim;
+  return fits ? kShapeTile256 : kShapeStream32;
 }
 
 int routed_tile_bound(int rows_total, int n_groups, int bm, int n, int bn) {
@@ -163,7 +176,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                     void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
                     const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
                     hipStream_t s) {
-  const int shape = expert_shape(d);
+  const int shape = expert_shape(d, perm != nullptr);
   const bool packed = d.weight_layout == MOE_LAYOUT_PACKED;
   const int bm = gemm_bm(shape);
   const int bn_gu = gemm_bn(true, shape), bn_dn = gemm_bn(false, shape);
@@ -264,7 +277,7 @@ int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, in
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.T == 0) return MOE_OK;
-  const int bm = gemm_bm(expert_shape(d));
+  const int bm = gemm_bm(expert_shape(d, true));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
                          at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm_token, inv_pos, bm, bm,
                          at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
@@ -352,7 +365,7 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm_token);
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
-  const int bm = gemm_bm(expert_shape(d));
+  const int bm = gemm_bm(expert_shape(d, true));
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
                          at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm, inv, bm, bm,
                          at<int32_t>(ws, L.tp_a),

@@ -39,6 +39,25 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
 
+// Raw buffer access: a wave-uniform 128-bit resource (base address, no stride, no range
+// limit in practice) plus a 32-bit per-lane offset and a 32-bit wave-uniform offset.
+// Loads through it need no per-lane 64-bit address arithmetic, so a loop can advance a
+// stream by changing only the uniform offset.  Word 3 is the gfx9-family default format
+// (32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  // readfirstlane returns int: each half goes back through uint32_t before widening, so
+  // an address with bit 31 set is not sign-extended into the upper half
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const uint64_t u = (static_cast<uint64_t>(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, -1, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------

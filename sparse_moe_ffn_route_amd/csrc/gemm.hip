@@ -34,6 +34,8 @@
 // matrix per wave halve the token bytes staged per MFMA; only experts with more rows
 // (skewed routing) take several M-tiles, adjacent in the launch order.
 // Tiles are ordered (group, N-tile, M-tile) and dealt to XCDs in contiguous ranges.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -124,6 +126,14 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     ks = (L / mt) % ksp;
     n_tile = L / mt / ksp;
   }
+  // the tile coordinates are wave-uniform; say so, so that addresses built from them
+  // stay in scalar registers
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  count = __builtin_amdgcn_readfirstlane(count);
+  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+  m = __builtin_amdgcn_readfirstlane(m);
+  ks = __builtin_amdgcn_readfirstlane(ks);
   const int rbeg = m * BM;
   const int nrows = min(BM, count - rbeg);
   const int N = SEL(N);
@@ -146,170 +156,320 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   const int ncol0 = n_tile * BN + wave * NF * 16;
   const int mf_active = (nrows + 15) / 16;
 
-  // ---- operand pointers ---------------------------------------------------
-  const uint8_t* wrow[NMAT][NF];
-#pragma unroll
-  for (int nf = 0; nf < NF; ++nf) {
-    size_t off;
-    if (PACKED) {
-      const int frag = min((ncol0 + nf * 16) / 16, N / 16 - 1);
-      off = (static_cast<size_t>(frag) * (Kb_row / 64) + kofs / 64) * 1024 + lane * 16;
-    } else {
-      const int n = min(ncol0 + nf * 16 + lrow, N - 1);
-      off = static_cast<size_t>(n) * Kb_row + kofs + lgrp * 16;
-    }
-    wrow[0][nf] = W0 + off;
-    if (SWIGLU) wrow[NMAT - 1][nf] = W1 + off;
-  }
-  const uint8_t* arow[CPT];
-  int acol[CPT], aoff[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = threadIdx.x + i * 256;
-    const int r = c / (KBLK / 16);
-    acol[i] = (c % (KBLK / 16)) * 16;
-    aoff[i] = r * LDS_ROW + acol[i];
-    arow[i] = nullptr;
-    if (r < nrows) {
-      const int grow = row0 + rbeg + r;
-      const int src = perm ? perm[grow] : grow;
-      arow[i] = A + static_cast<size_t>(src) * lda_b;
-    }
-  }
-
-  f32x4 acc[NMAT][NF][MF];
-#pragma unroll
-  for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // Full K blocks run a branch-free pipeline; a last partial block (K*ES not a
-  // multiple of KBLK, only in small shapes) is handled after it with per-step guards.
+  // multiple of KBLK) is handled after it with per-step guards.
   const int nfull = Kb / KBLK;
   const int tail_steps = (Kb - nfull * KBLK) / 64;
 
-  // Loads of K block kb; past the last block (kb >= nfull) every lane reads the same
-  // 64 bytes at the start of the first token row instead, which stay in L2, so the
-  // ring's tail prefetch costs no memory traffic and the loop needs no branch.
-  const uint8_t* dummy = A + (lane & 3) * 16;
-  auto load_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
-    const bool real = kb < nfull;
-    const size_t off = static_cast<size_t>(real ? kb : 0) * SBLK;
+  // ---- epilogue: scales, SwiGLU, store --------------------------------------
+  auto epilogue = [&](const f32x4 (&acc)[NMAT][NF][MF]) {
+    void* out = static_cast<uint8_t*>(SEL(out)) + static_cast<size_t>(ks) * SEL(out_split_stride) * (OUT == EL_F32 ? 4 : 2);
+    const size_t ldo = SEL(ldo);
+    const float* a_scale = SEL(a_scale);
+    const float* s0 = SEL(s0);
+    const float* s1 = SEL(s1);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+    for (int mf = 0; mf < MF; ++mf) {
+      const int r = mf * 16 + lrow;
+      if (r >= nrows) continue;
+      const int grow = row0 + rbeg + r;
+      float as = 1.0f;
+      if (EL == EL_E4M3) as = a_scale[perm ? perm[grow] : grow];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const int n = ncol0 + nf * 16 + lgrp * 4;
+        if (n >= N) continue;
+        const int valid = min(4, N - n);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x0 = acc[0][nf][mf][i];
+          if (EL == EL_E4M3) x0 *= as * s0[static_cast<size_t>(g) * N + min(n + i, N - 1)];
+          if (SWIGLU) {
+            float x1 = acc[NMAT - 1][nf][mf][i];
+            if (EL == EL_E4M3) x1 *= as * s1[static_cast<size_t>(g) * N + min(n + i, N - 1)];
+            v[i] = silu(x0) * x1;
+          } else {
+            v[i] = x0;
+          }
+        }
+        OutStore<OUT>::store4(out, static_cast<size_t>(grow) * ldo + n, v, valid);
+      }
+    }
+  };
+
+  if constexpr (MF >= 8) {
+    // ---- tile shape ---------------------------------------------------------
+    // Weights and token rows are read through buffer resources: a wave-uniform base, a
+    // fixed 32-bit offset per lane, and the K-block offset as the uniform part, so the
+    // loop computes no per-lane addresses (the host keeps every offset below 2^31).
+    // Token rows past the tile's last row re-read its last row (harmless: those output
+    // rows are never stored), so every load in the loop is unconditional.  The K loop
+    // is specialised on the number of 16-row fragments actually in use (rounded up to a
+    // multiple of kFragGroup), so the fragment loop has no branches and the LDS reads
+    // run one fragment ahead of the MFMAs.
+    static_assert(!NTW, "the tile shape streams weights through the cache");
+    constexpr int kFragGroup = 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int ncol0u = n_tile * BN + wv * NF * 16;
+    __amdgpu_buffer_rsrc_t wres[NMAT];
+    wres[0] = buffer_rsrc(W0);
+    if (SWIGLU) wres[NMAT - 1] = buffer_rsrc(W1);
+    uint32_t woff_v[NF], woff_s[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      if (PACKED) {
+        const int frag = min((ncol0u + nf * 16) / 16, N / 16 - 1);
+        woff_s[nf] = (static_cast<uint32_t>(frag) * (Kb_row / 64) + kofs / 64) * 1024;
+        woff_v[nf] = lane * 16;
+      } else {
+        const int n = min(ncol0u + nf * 16 + lrow, N - 1);
+        woff_s[nf] = kofs;
+        woff_v[nf] = static_cast<uint32_t>(n) * Kb_row + lgrp * 16;
+      }
+    }
+    constexpr int CPR = KBLK / 16;        // 16-byte chunks per token row per K block
+    constexpr int RPP = 256 / CPR;        // token rows per pass of the workgroup
+    constexpr int NTP = BM / RPP;         // passes for a full tile
+    const int crow = threadIdx.x / CPR, ccol = (threadIdx.x % CPR) * 16;
+    const __amdgpu_buffer_rsrc_t tres = buffer_rsrc(A);
+    uint32_t toff[NTP];
+#pragma unroll
+    for (int i = 0; i < NTP; ++i) {
+      const int grow = row0 + rbeg + min(crow + i * RPP, nrows - 1);
+      toff[i] = static_cast<uint32_t>(perm ? perm[grow] : grow) * static_cast<uint32_t>(lda_b) + ccol;
+    }
+    const int tl_off = crow * LDS_ROW + ccol;
+    const int b_off = lrow * LDS_ROW + lgrp * 16;
+
+    auto run = [&](auto mfr_c) {
+      constexpr int MFR = decltype(mfr_c)::value;      // fragments computed
+      constexpr int NTL = (MFR * 16 + RPP - 1) / RPP;  // token passes they need
+      f32x4 acc[NMAT][NF][MF];
 #pragma unroll
       for (int a = 0; a < NMAT; ++a)
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
-          w[a][nf][s] = load_weight<NTW>(real ? wrow[a][nf] + off + s * SSTEP : dummy);
-  };
-  auto load_a = [&](u32x4 (&av)[CPT], int kb, int bytes) {
-    const int off = kb * KBLK;
+#pragma unroll
+          for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x4 wr[NBUF][NMAT][NF][KSTEPS];
+      u32x4 tv[NTL];
+      auto ld_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
+        const uint32_t o = static_cast<uint32_t>(min(kb, nfull - 1)) * SBLK;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+          for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+              w[a][nf][st] = buffer_load16(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
+      };
+      auto ld_t = [&](int kb) {
+        const uint32_t o = static_cast<uint32_t>(min(kb, nfull - 1)) * KBLK;
+#pragma unroll
+        for (int i = 0; i < NTL; ++i) tv[i] = buffer_load16(tres, toff[i], o);
+      };
+      auto st_t = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NTL; ++i) *reinterpret_cast<u32x4*>(&sA[buf][tl_off + i * RPP * LDS_ROW]) = tv[i];
+      };
+      // Token fragments are read one ahead of the MFMAs that use them; the scheduling
+      // barriers keep that order (the scheduler would otherwise hoist every read of the
+      // block and run out of registers).
+      auto mm = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int nst) {
+        const uint8_t* sb = &sA[buf][b_off];
+        u32x4 bq[2];
+        bq[0] = *reinterpret_cast<const u32x4*>(sb);
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+          if (st >= nst) break;
+#pragma unroll
+          for (int mf = 0; mf < MFR; ++mf) {
+            const int nx = st * MFR + mf + 1;  // next (step, fragment) in issue order
+            if (nx < KSTEPS * MFR && (nx / MFR) < nst)
+              bq[nx & 1] = *reinterpret_cast<const u32x4*>(sb + (nx % MFR) * 16 * LDS_ROW + (nx / MFR) * 64);
+#pragma unroll
+            for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+              for (int nf = 0; nf < NF; ++nf)
+                acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][st], bq[(nx - 1) & 1], acc[a][nf][mf]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      };
+      if (nfull > 0) {
+        ld_t(0);
+#pragma unroll
+        for (int j = 0; j < NBUF - 1; ++j) ld_w(wr[j], j);
+        st_t(0);
+        __syncthreads();
+        for (int kb = 0; kb < nfull; kb += NBUF) {
+#pragma unroll
+          for (int j = 0; j < NBUF; ++j) {
+            if (j > 0 && kb + j >= nfull) break;
+            ld_t(kb + j + 1);
+            ld_w(wr[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
+            mm(wr[j], (kb + j) & 1, KSTEPS);
+            st_t((kb + j + 1) & 1);
+            __syncthreads();
+          }
+        }
+      }
+      if (tail_steps > 0) {
+        const int buf = nfull & 1;
+        const int tb = tail_steps * 64;
+#pragma unroll
+        for (int i = 0; i < NTL; ++i)
+          tv[i] = ccol < tb ? buffer_load16(tres, toff[i], nfull * KBLK) : u32x4{0u, 0u, 0u, 0u};
+        st_t(buf);
+        const uint32_t o = static_cast<uint32_t>(nfull) * SBLK;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+          for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+              if (st < tail_steps) wr[0][a][nf][st] = buffer_load16(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
+        __syncthreads();
+        mm(wr[0], buf, tail_steps);
+      }
+      epilogue(acc);
+    };
+    static_assert(MF % kFragGroup == 0, "tile height must be whole fragment groups");
+    switch ((mf_active + kFragGroup - 1) / kFragGroup) {
+      case 1: run(std::integral_constant<int, kFragGroup>{}); break;
+      case 2: run(std::integral_constant<int, 2 * kFragGroup < MF ? 2 * kFragGroup : MF>{}); break;
+      case 3: run(std::integral_constant<int, 3 * kFragGroup < MF ? 3 * kFragGroup : MF>{}); break;
+      default: run(std::integral_constant<int, MF>{}); break;
+    }
+  } else {
+    // ---- streaming shapes -----------------------------------------------------
+    f32x4 acc[NMAT][NF][MF];
+#pragma unroll
+    for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- operand pointers ---------------------------------------------------
+    const uint8_t* wrow[NMAT][NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      size_t off;
+      if (PACKED) {
+        const int frag = min((ncol0 + nf * 16) / 16, N / 16 - 1);
+        off = (static_cast<size_t>(frag) * (Kb_row / 64) + kofs / 64) * 1024 + lane * 16;
+      } else {
+        const int n = min(ncol0 + nf * 16 + lrow, N - 1);
+        off = static_cast<size_t>(n) * Kb_row + kofs + lgrp * 16;
+      }
+      wrow[0][nf] = W0 + off;
+      if (SWIGLU) wrow[NMAT - 1][nf] = W1 + off;
+    }
+    const uint8_t* arow[CPT];
+    int acol[CPT], aoff[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      av[i] = u32x4{0u, 0u, 0u, 0u};
-      if (arow[i] && acol[i] < bytes) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + off + acol[i]);
+      const int c = threadIdx.x + i * 256;
+      const int r = c / (KBLK / 16);
+      acol[i] = (c % (KBLK / 16)) * 16;
+      aoff[i] = r * LDS_ROW + acol[i];
+      arow[i] = nullptr;
+      if (r < nrows) {
+        const int grow = row0 + rbeg + r;
+        const int src = perm ? perm[grow] : grow;
+        arow[i] = A + static_cast<size_t>(src) * lda_b;
+      }
     }
-  };
-  auto store_a = [&](const u32x4 (&av)[CPT], int buf) {
+
+
+    // Loads of K block kb; past the last block (kb >= nfull) every lane reads the same
+    // 64 bytes at the start of the first token row instead, which stay in L2, so the
+    // ring's tail prefetch costs no memory traffic and the loop needs no branch.
+    const uint8_t* dummy = A + (lane & 3) * 16;
+    auto load_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
+      const bool real = kb < nfull;
+      const size_t off = static_cast<size_t>(real ? kb : 0) * SBLK;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&sA[buf][aoff[i]]) = av[i];
-  };
-  auto step = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int s) {
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      if (MF == 1 || mf < mf_active) {
-        const u32x4 bfr =
-            *reinterpret_cast<const u32x4*>(&sA[buf][(mf * 16 + lrow) * LDS_ROW + s * 64 + lgrp * 16]);
+      for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int a = 0; a < NMAT; ++a)
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf) acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][s], bfr, acc[a][nf][mf]);
+          for (int nf = 0; nf < NF; ++nf)
+            w[a][nf][s] = load_weight<NTW>(real ? wrow[a][nf] + off + s * SSTEP : dummy);
+    };
+    auto load_a = [&](u32x4 (&av)[CPT], int kb, int bytes) {
+      const int off = kb * KBLK;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        av[i] = u32x4{0u, 0u, 0u, 0u};
+        if (arow[i] && acol[i] < bytes) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + off + acol[i]);
       }
-    }
-  };
-  auto compute = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf) {
+    };
+    auto store_a = [&](const u32x4 (&av)[CPT], int buf) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) step(w, buf, s);
-  };
-
-  // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
-  // NBUF - 1 blocks before it is multiplied.  Prefetches past the last block read the
-  // L2-resident dummy instead of being guarded, so the loop body has no data-dependent
-  // branches.
-  u32x4 wb[NBUF][NMAT][NF][KSTEPS];
-  u32x4 av[CPT];
-  if (nfull > 0) {
-    load_a(av, 0, KBLK);
+      for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&sA[buf][aoff[i]]) = av[i];
+    };
+    auto step = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int s) {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], j);
-    store_a(av, 0);
-    __syncthreads();
-    for (int kb = 0; kb < nfull; kb += NBUF) {
+      for (int mf = 0; mf < MF; ++mf) {
+        if (MF == 1 || mf < mf_active) {
+          const u32x4 bfr =
+              *reinterpret_cast<const u32x4*>(&sA[buf][(mf * 16 + lrow) * LDS_ROW + s * 64 + lgrp * 16]);
 #pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        if (j > 0 && kb + j >= nfull) break;
-        load_a(av, min(kb + j + 1, nfull - 1), KBLK);
-        load_w(wb[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
-        compute(wb[j], (kb + j) & 1);
-        store_a(av, (kb + j + 1) & 1);
-        __syncthreads();
-      }
-    }
-  }
-  if (tail_steps > 0) {
-    const int buf = nfull & 1;
-    load_a(av, nfull, tail_steps * 64);
-    store_a(av, buf);
-    const size_t off = static_cast<size_t>(nfull) * SBLK;
+          for (int a = 0; a < NMAT; ++a)
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-      for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * SSTEP);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      if (s < tail_steps) step(wb[0], buf, s);
-  }
-
-  // ---- epilogue -------------------------------------------------------------
-  void* out = static_cast<uint8_t*>(SEL(out)) + static_cast<size_t>(ks) * SEL(out_split_stride) * (OUT == EL_F32 ? 4 : 2);
-  const size_t ldo = SEL(ldo);
-  const float* a_scale = SEL(a_scale);
-  const float* s0 = SEL(s0);
-  const float* s1 = SEL(s1);
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    const int r = mf * 16 + lrow;
-    if (r >= nrows) continue;
-    const int grow = row0 + rbeg + r;
-    float as = 1.0f;
-    if (EL == EL_E4M3) as = a_scale[perm ? perm[grow] : grow];
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf) {
-      const int n = ncol0 + nf * 16 + lgrp * 4;
-      if (n >= N) continue;
-      const int valid = min(4, N - n);
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x0 = acc[0][nf][mf][i];
-        if (EL == EL_E4M3) x0 *= as * s0[static_cast<size_t>(g) * N + min(n + i, N - 1)];
-        if (SWIGLU) {
-          float x1 = acc[NMAT - 1][nf][mf][i];
-          if (EL == EL_E4M3) x1 *= as * s1[static_cast<size_t>(g) * N + min(n + i, N - 1)];
-          v[i] = silu(x0) * x1;
-        } else {
-          v[i] = x0;
+            for (int nf = 0; nf < NF; ++nf) acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][s], bfr, acc[a][nf][mf]);
         }
       }
-      OutStore<OUT>::store4(out, static_cast<size_t>(grow) * ldo + n, v, valid);
+    };
+    auto compute = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) step(w, buf, s);
+    };
+
+    // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
+    // NBUF - 1 blocks before it is multiplied.  Prefetches past the last block read the
+    // L2-resident dummy instead of being guarded, so the loop body has no data-dependent
+    // branches.
+    u32x4 wb[NBUF][NMAT][NF][KSTEPS];
+    u32x4 av[CPT];
+    if (nfull > 0) {
+      load_a(av, 0, KBLK);
+#pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], j);
+      store_a(av, 0);
+      __syncthreads();
+      for (int kb = 0; kb < nfull; kb += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          if (j > 0 && kb + j >= nfull) break;
+          load_a(av, min(kb + j + 1, nfull - 1), KBLK);
+          load_w(wb[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
+          compute(wb[j], (kb + j) & 1);
+          store_a(av, (kb + j + 1) & 1);
+          __syncthreads();
+        }
+      }
     }
+    if (tail_steps > 0) {
+      const int buf = nfull & 1;
+      load_a(av, nfull, tail_steps * 64);
+      store_a(av, buf);
+      const size_t off = static_cast<size_t>(nfull) * SBLK;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * SSTEP);
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < tail_steps) step(wb[0], buf, s);
+    }
+    epilogue(acc);
   }
 #undef SEL
 }
