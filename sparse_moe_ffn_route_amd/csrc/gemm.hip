@@ -70,13 +70,16 @@ template <> struct OutStore<EL_BF16> {
   }
 };
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load_weight(const uint8_t* p) {
   if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED>
+template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED,
+          int TDEPTH>
 __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmProblem p1, int has_p1) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
@@ -208,8 +211,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     // is specialised on the number of 16-row fragments actually in use (rounded up to a
     // multiple of kFragGroup), so the fragment loop has no branches and the LDS reads
     // run one fragment ahead of the MFMAs.
-    static_assert(!NTW, "the tile shape streams weights through the cache");
-    constexpr int kFragGroup = 4;
+    constexpr int kFragGroup = 2;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int ncol0u = n_tile * BN + wv * NF * 16;
     __amdgpu_buffer_rsrc_t wres[NMAT];
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 #pragma unroll
           for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
       u32x4 wr[NBUF][NMAT][NF][KSTEPS];
-      u32x4 tv[NTL];
+      u32x4 tv[TDEPTH][NTL];  // token rows of the next TDEPTH blocks, in flight
       auto ld_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
         const uint32_t o = static_cast<uint32_t>(min(kb, nfull - 1)) * SBLK;
 #pragma unroll
@@ -262,55 +264,74 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
           for (int a = 0; a < NMAT; ++a)
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf)
-              w[a][nf][st] = buffer_load16(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
+              w[a][nf][st] = buffer_load16<NTW>(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
       };
-      auto ld_t = [&](int kb) {
+      auto ld_t = [&](u32x4 (&t)[NTL], int kb) {
         const uint32_t o = static_cast<uint32_t>(min(kb, nfull - 1)) * KBLK;
 #pragma unroll
-        for (int i = 0; i < NTL; ++i) tv[i] = buffer_load16(tres, toff[i], o);
+        for (int i = 0; i < NTL; ++i) t[i] = buffer_load16(tres, toff[i], o);
       };
-      auto st_t = [&](int buf) {
+      auto st_t = [&](const u32x4 (&t)[NTL], int buf) {
 #pragma unroll
-        for (int i = 0; i < NTL; ++i) *reinterpret_cast<u32x4*>(&sA[buf][tl_off + i * RPP * LDS_ROW]) = tv[i];
+        for (int i = 0; i < NTL; ++i) *reinterpret_cast<u32x4*>(&sA[buf][tl_off + i * RPP * LDS_ROW]) = t[i];
       };
-      // Token fragments are read one ahead of the MFMAs that use them; the scheduling
-      // barriers keep that order (the scheduler would otherwise hoist every read of the
-      // block and run out of registers).
+      // Token fragments are read kLdsAhead fragments ahead of the MFMAs that use them
+      // (a ring of kLdsAhead + 1 registers); the scheduling barriers keep that order
+      // (the scheduler would otherwise hoist every read of the block and run out of
+      // registers).
+      constexpr int kLdsAhead = 1;
+      constexpr int NQ = kLdsAhead + 1;
       auto mm = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int nst) {
         const uint8_t* sb = &sA[buf][b_off];
-        u32x4 bq[2];
-        bq[0] = *reinterpret_cast<const u32x4*>(sb);
+        const int total = nst * MFR;  // (step, fragment) pairs of this block, in issue order
+        auto frag_at = [&](int q) {
+          return *reinterpret_cast<const u32x4*>(sb + (q % MFR) * 16 * LDS_ROW + (q / MFR) * 64);
+        };
+        u32x4 bq[NQ];
+#pragma unroll
+        for (int q = 0; q < kLdsAhead; ++q)
+          if (q < KSTEPS * MFR && q < total) bq[q] = frag_at(q);
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
           if (st >= nst) break;
 #pragma unroll
           for (int mf = 0; mf < MFR; ++mf) {
-            const int nx = st * MFR + mf + 1;  // next (step, fragment) in issue order
-            if (nx < KSTEPS * MFR && (nx / MFR) < nst)
-              bq[nx & 1] = *reinterpret_cast<const u32x4*>(sb + (nx % MFR) * 16 * LDS_ROW + (nx / MFR) * 64);
+            const int cur = st * MFR + mf;
+            const int nx = cur + kLdsAhead;
+            if (nx < KSTEPS * MFR && nx < total) bq[nx % NQ] = frag_at(nx);
 #pragma unroll
             for (int a = 0; a < NMAT; ++a)
 #pragma unroll
               for (int nf = 0; nf < NF; ++nf)
-                acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][st], bq[(nx - 1) & 1], acc[a][nf][mf]);
+                acc[a][nf][mf] = mfma_chunk<EL>(w[a][nf][st], bq[cur % NQ], acc[a][nf][mf]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       };
+      // Block b's token rows are loaded TDEPTH blocks ahead into tv[b % TDEPTH] and
+      // stored to LDS buffer b & 1 at the end of block b - 1; its weights are loaded
+      // NBUF - 1 blocks ahead into wr[b % NBUF].  The loop is unrolled over
+      // lcm(NBUF, TDEPTH) blocks so both ring indices are compile-time constants.
+      // Loads complete in issue order, so waiting for a block's token rows also waits
+      // for every older load: with TDEPTH = NBUF - 1 the token rows of block b + 1 are
+      // issued together with its weights, and that wait never holds up a weight
+      // prefetch that is still needed later.
+      constexpr int U = NBUF * TDEPTH / gcd_c(NBUF, TDEPTH);
       if (nfull > 0) {
-        ld_t(0);
+#pragma unroll
+        for (int d = 0; d < TDEPTH; ++d) ld_t(tv[d], d);
 #pragma unroll
         for (int j = 0; j < NBUF - 1; ++j) ld_w(wr[j], j);
-        st_t(0);
+        st_t(tv[0], 0);
         __syncthreads();
-        for (int kb = 0; kb < nfull; kb += NBUF) {
+        for (int kb = 0; kb < nfull; kb += U) {
 #pragma unroll
-          for (int j = 0; j < NBUF; ++j) {
+          for (int j = 0; j < U; ++j) {
             if (j > 0 && kb + j >= nfull) break;
-            ld_t(kb + j + 1);
+            ld_t(tv[j % TDEPTH], kb + j + TDEPTH);
             ld_w(wr[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
-            mm(wr[j], (kb + j) & 1, KSTEPS);
-            st_t((kb + j + 1) & 1);
+            mm(wr[j % NBUF], (kb + j) & 1, KSTEPS);
+            st_t(tv[(j + 1) % TDEPTH], (kb + j + 1) & 1);
             __syncthreads();
           }
         }
@@ -320,8 +341,8 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
         const int tb = tail_steps * 64;
 #pragma unroll
         for (int i = 0; i < NTL; ++i)
-          tv[i] = ccol < tb ? buffer_load16(tres, toff[i], nfull * KBLK) : u32x4{0u, 0u, 0u, 0u};
-        st_t(buf);
+          tv[0][i] = ccol < tb ? buffer_load16(tres, toff[i], nfull * KBLK) : u32x4{0u, 0u, 0u, 0u};
+        st_t(tv[0], buf);
         const uint32_t o = static_cast<uint32_t>(nfull) * SBLK;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st)
@@ -329,7 +350,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
           for (int a = 0; a < NMAT; ++a)
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf)
-              if (st < tail_steps) wr[0][a][nf][st] = buffer_load16(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
+              if (st < tail_steps) wr[0][a][nf][st] = buffer_load16<NTW>(wres[a], woff_v[nf], woff_s[nf] + o + st * SSTEP);
         __syncthreads();
         mm(wr[0], buf, tail_steps);
       }
@@ -340,6 +361,10 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
       case 1: run(std::integral_constant<int, kFragGroup>{}); break;
       case 2: run(std::integral_constant<int, 2 * kFragGroup < MF ? 2 * kFragGroup : MF>{}); break;
       case 3: run(std::integral_constant<int, 3 * kFragGroup < MF ? 3 * kFragGroup : MF>{}); break;
+      case 4: run(std::integral_constant<int, 4 * kFragGroup < MF ? 4 * kFragGroup : MF>{}); break;
+      case 5: run(std::integral_constant<int, 5 * kFragGroup < MF ? 5 * kFragGroup : MF>{}); break;
+      case 6: run(std::integral_constant<int, 6 * kFragGroup < MF ? 6 * kFragGroup : MF>{}); break;
+      case 7: run(std::integral_constant<int, 7 * kFragGroup < MF ? 7 * kFragGroup : MF>{}); break;
       default: run(std::integral_constant<int, MF>{}); break;
     }
   } else {
@@ -481,16 +506,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 // 128-byte line is split over two load instructions, and the hint costs bandwidth.
 template <int SHAPE, bool SWIGLU, bool PACKED> struct Shape;
 template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream16, SWIGLU, PACKED> {
-  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, NBUF = 2, MINB = 2;
+  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, NBUF = 2, MINB = 2, TDEPTH = 1;
   static constexpr bool NT = PACKED;
 };
 template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream32, SWIGLU, PACKED> {
-  static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2;
+  static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2, TDEPTH = 1;
   static constexpr bool NT = PACKED;
 };
 template <bool SWIGLU, bool PACKED> struct Shape<kShapeTile256, SWIGLU, PACKED> {
-  static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1;
-  static constexpr bool NT = false;
+  static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1, TDEPTH = 2;
+  static constexpr bool NT = PACKED;
 };
 
 template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
@@ -506,7 +531,7 @@ hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tile
   }
   const int grid = max_tiles0 + tiles1;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED>),
+  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH>),
                      dim3(grid), dim3(256), 0, stream, p0, q1, p1 ? 1 : 0);
   return hipGetLastError();
 }
