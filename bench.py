@@ -6,12 +6,16 @@ expert, grouped gate/up SwiGLU GEMM with the shared expert, grouped down GEMM,
 weighted combine) over one batch, through the C-ABI entry moe_layer_forward.
 Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM before
 the timed region.  The primary line is the 512-token decode batch (D=4096,
-512 experts of I=1024, top-10, one shared expert of I=1024, bf16); the
-8192-token prefill chunk of the same layer is measured in the same run.
+512 experts of I=1024, top-10, one shared expert of I=1024, bf16).  The same
+run also measures ("secondary") the 8192-token prefill chunk of that layer, the
+skewed-popularity prefill, one GPU's fp8 expert-parallel share (64 of 512
+experts, routing given) and the tiny fp32 layer.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the grouped
 gate/up GEMM), timed live with HIP events recorded on the launch stream around
-it in every timed step; `cpu_baseline` times the CPU oracle on the host cores.
+it in every timed step; `measured_peaks` is the streaming-read bandwidth of a
+plain read kernel on the same device; `cpu_baseline` times the CPU oracle on
+the host cores.
 """
 
 import argparse
@@ -35,14 +39,15 @@ _ES = {"f32": 4, "bf16": 2, "e4m3": 1}
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_bf16")
     p.add_argument("--layout", default="packed", choices=["packed", "rows"],
                    help="expert weight layout (packed: repacked once by moe_pack_weights before timing)")
-    p.add_argument("--secondary", default="prefill_bf16",
-                   help="second workload measured with the same weights ('' to skip)")
-    p.add_argument("--secondary-steps", type=int, default=5)
+    p.add_argument("--secondary", default="prefill_bf16,skew_prefill_bf16,ep_share_fp8,tiny_fp32",
+                   help="comma-separated workloads also measured ('' for none); the bf16 ones reuse the weights")
+    p.add_argument("--secondary-steps", type=int, default=20)
+    p.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming-read bandwidth probe")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens of the oracle sample (0: whole batch)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -115,9 +120,11 @@ class Layer:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         stages = {name: [] for name in self.moe.STAGES}
+        self.step_ms = []
         for evs in ev_sets:
             for j, name in enumerate(self.moe.STAGES):
                 stages[name].append(evs[j].elapsed_time(evs[j + 1]))
+            self.step_ms.append(evs[0].elapsed_time(evs[-1]))
         return wall, {k: sum(v) / len(v) for k, v in stages.items()}
 
     # ---- algorithmic work ---------------------------------------------------
@@ -158,7 +165,10 @@ def layer_summary(layer, wall, stages, steps):
     peak_tf = FP8_PEAK_TFLOPS if wl.w == "e4m3" else BF16_PEAK_TFLOPS
     hbm_frac = w["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     mfma_frac = w["layer_flop"] / (ms * 1e-3) / 1e12 / peak_tf
+    q = sorted(layer.step_ms)
+    pick = lambda f: round(q[min(len(q) - 1, int(f * (len(q) - 1) + 0.5))], 4)
     return dict(workload=wl.name, tokens_per_s=wl.T / (ms * 1e-3), ms_per_step=ms,
+                step_ms_events={"p10": pick(0.1), "median": pick(0.5), "p90": pick(0.9), "n": len(q)},
                 layer_hbm_frac=hbm_frac, layer_mfma_frac=mfma_frac,
                 layer_roofline_frac=max(hbm_frac, mfma_frac), stage_ms=stages, work=w)
 
@@ -167,10 +177,12 @@ def roofline_of(layer, stages):
     w = layer.work()
     t = stages["gate_up"] * 1e-3
     achieved = w["gate_up_bytes"] / t / 1e9
+    shared = " + shared expert" if layer.wl.I_shared else ""
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(layer.wl.name),
-            "kernel": "gemm_kernel<bf16,SwiGLU> (grouped gate/up + shared expert)",
-            "bytes_per_launch": w["gate_up_bytes"], "avg_launch_ms": round(stages["gate_up"], 4)}
+            "kernel": f"gemm_kernel<{layer.wl.w},SwiGLU> (grouped gate/up{shared})",
+            "bytes_per_launch": w["gate_up_bytes"], "avg_launch_ms": round(stages["gate_up"], 4),
+            "mfma_TFLOPs": round(w["gate_up_flop"] / t / 1e12, 1)}
 
 
 def cpu_baseline(layer, sample_tokens):
@@ -229,6 +241,24 @@ def copy_probe(mib):
     return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}
 
 
+def hbm_probe(buf, reps=5):
+    """Best-of-reps streaming-read bandwidth (GB/s) of moe_hbm_read_probe over buf."""
+    import torch
+    import sparse_moe_ffn_route_amd as moe
+    nbytes = buf.numel() * buf.element_size()
+    nbytes -= nbytes % 16
+    sink = torch.empty(moe.HBM_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_hbm_read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    return round(best, 1)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -260,24 +290,41 @@ def main():
     print(f"[bench] {wl.name}: {prim['ms_per_step']:.3f} ms/step, stages {stages}", file=sys.stderr, flush=True)
 
     secondary = []
-    if args.secondary:
-        wl2 = synth.WORKLOADS[args.secondary]
+    for name in [n for n in args.secondary.split(",") if n]:
+        wl2 = synth.WORKLOADS[name]
         same_layer = all(getattr(wl2, f) == getattr(wl, f) for f in ("D", "E", "I", "I_shared", "w", "act"))
-        if same_layer:
-            # same weights; new hidden states of the secondary batch size
+        if same_layer and not wl2.routing_given:
+            # same weights; new hidden states of the batch size (and the workload's logit bias)
             g = torch.Generator(device="cuda")
             g.manual_seed(synth._torch_seed(0, "x", 1))
             x2 = (torch.randn(wl2.T, wl2.D, generator=g, device="cuda")).to(torch.bfloat16)
+            bias = None
+            if wl2.skew_alpha is not None:
+                bias = torch.from_numpy(synth.zipf_bias(wl2.E, wl2.skew_alpha, wl2.skew_s, wl2.skew_empty, 1)).cuda()
             inp2 = synth.LayerInputs(wl2, x2, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
-                                     inp.s_down, inp.ws_gate, inp.ws_up, inp.ws_down, None, None)
-            layer2 = Layer(wl2, inp2, packed_w)
-            wall2, stages2 = layer2.run(args.secondary_steps, 2)
-            sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
-            sec["roofline"] = roofline_of(layer2, stages2)
-            secondary.append(sec)
-            print(f"[bench] {wl2.name}: {sec['ms_per_step']:.3f} ms/step, stages {stages2}", file=sys.stderr,
-                  flush=True)
-            del layer2, inp2, x2
+                                     inp.s_down, inp.ws_gate, inp.ws_up, inp.ws_down, bias, None)
+            pw2 = packed_w
+        else:
+            inp2 = synth.make_inputs(wl2, seed=0, device="cuda")
+            pw2 = None
+            if args.layout == "packed":
+                import sparse_moe_ffn_route_amd as moe
+                pw2 = {n: (None if getattr(inp2, n) is None else moe.moe_pack_weights(getattr(inp2, n)))
+                       for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+        layer2 = Layer(wl2, inp2, pw2)
+        wall2, stages2 = layer2.run(args.secondary_steps, 2)
+        sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
+        sec["roofline"] = roofline_of(layer2, stages2)
+        secondary.append(sec)
+        print(f"[bench] {wl2.name}: {sec['ms_per_step']:.3f} ms/step, stages {stages2}", file=sys.stderr, flush=True)
+        del layer2, inp2, pw2
+        torch.cuda.empty_cache()
+
+    measured = None
+    if not args.no_hbm_probe:
+        measured = {"hbm_read_GBs": hbm_probe(packed_w["w_gate"] if packed_w else inp.w_gate),
+                    "how": "moe_hbm_read_probe over the expert gate weights (non-temporal 16-byte loads), best of 5"}
+        print(f"[bench] streaming read: {measured['hbm_read_GBs']} GB/s", file=sys.stderr, flush=True)
 
     probe = copy_probe(args.copy_probe_mib) if args.copy_probe_mib else None
 
@@ -305,11 +352,15 @@ def main():
                    "weight_layout": args.layout, "parallelism": "1 GPU"},
         "roofline": roofline_of(layer, stages),
         "cpu_baseline": cpu,
-        "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_roofline_frac", "stage_ms")},
+        "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_roofline_frac", "stage_ms",
+                                        "step_ms_events")},
         "work": prim["work"],
         "secondary": secondary,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if measured:
+        out["measured_peaks"] = measured
+        out["roofline"]["frac_of_measured_hbm"] = round(out["roofline"]["achieved"] / measured["hbm_read_GBs"], 4)
     if probe:
         out["copy_probe"] = probe
     print(json.dumps(out))

@@ -235,6 +235,17 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const vo
 int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst,
                      void* stream);
 
+/*
+ * Measurement helper, not part of the layer: reads `bytes` (a multiple of 16) of device
+ * memory at buf once with wide non-temporal loads and writes 16384 uint32 words of XOR
+ * checksums into sink (device, caller-owned, at least 16384 words).  Timing it over a
+ * buffer much larger than the caches gives the achievable HBM read bandwidth that the
+ * grouped GEMMs' weight streams are compared with.  Asynchronous on stream.  Returns
+ * MOE_ERR_UNSUPPORTED if bytes is not a multiple of 16, MOE_ERR_NULL_ARG for NULL
+ * pointers (bytes > 0).
+ */
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable text of a moe_status code (static storage). */
 const char* moe_status_string(int status);
 

@@ -34,7 +34,8 @@ OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1,
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine",
-    "moe_layer_forward", "moe_pack_weights", "moe_status_string", "moe_last_hip_error", "moe_abi_version",
+    "moe_layer_forward", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
+    "moe_abi_version",
 )
 
 
@@ -82,6 +83,8 @@ def library() -> ctypes.CDLL:
     lib.moe_layer_forward.restype = i32
     lib.moe_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_pack_weights.restype = i32
+    lib.moe_hbm_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.moe_hbm_read_probe.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_hip_error.argtypes = []
@@ -207,6 +210,21 @@ def moe_pack_weights(src: torch.Tensor, dst: Optional[torch.Tensor] = None, stre
     _check(library().moe_pack_weights(_CODE_OF_TORCH[src.dtype], n, rows, cols, _ptr(src), _ptr(dst),
                                       _stream(stream)), "moe_pack_weights")
     return dst
+
+
+HBM_PROBE_SINK_WORDS = 16384
+
+
+def moe_hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Read all of buf once (measurement helper); returns the checksum words."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(HBM_PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    if sink.numel() * sink.element_size() < HBM_PROBE_SINK_WORDS * 4:
+        raise ValueError("sink must hold 16384 32-bit words")
+    _check(library().moe_hbm_read_probe(_ptr(buf), nbytes - nbytes % 16, _ptr(sink), _stream(stream)),
+           "moe_hbm_read_probe")
+    return sink
 
 
 def torch_dtype(code: int) -> torch.dtype:

@@ -406,6 +406,13 @@ int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, 
                                 static_cast<hipStream_t>(stream)));
 }
 
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16) return MOE_ERR_UNSUPPORTED;
+  if (bytes == 0) return MOE_OK;
+  if (!buf || !sink) return MOE_ERR_NULL_ARG;
+  return hip_status(launch_read_probe(buf, static_cast<int64_t>(bytes), sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -84,6 +84,11 @@ hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, 
                        const GemmProblem* p1, int max_tiles0, hipStream_t stream);
 
 // Repack n_mats row-major [rows][row_bytes] matrices into the fragment-major layout.
+// Streaming read of bytes (multiple of 16) at src; sink receives one word per workgroup
+// (at most kReadProbeBlocks workgroups).
+constexpr int kReadProbeBlocks = 16384;
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 hipError_t launch_pack(const void* src, void* dst, int64_t n_mats, int rows, int row_bytes, hipStream_t stream);
 
 hipError_t launch_combine(int out_el, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,

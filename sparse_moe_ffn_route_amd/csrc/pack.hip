@@ -1,3 +1,6 @@
+// Weight repacking, and a plain streaming-read kernel for measuring achievable HBM
+// bandwidth on the running device.
+//
 // One-time repacking of weight matrices into the fragment-major order the grouped GEMM
 // streams (see moe_pack_weights in moe.h): for output-row fragment f (16 rows) and
 // 64-byte reduction slice s, bytes [s*64, s*64+64) of rows 16f .. 16f+15 form one
@@ -29,7 +32,51 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ s
   }
 }
 
+// Each wave reads its own contiguous span of span16 16-byte chunks front to back, one
+// 1 KB row of the wave per load and kReadUnroll loads in flight (non-temporal), the way
+// a GEMM wave walks its packed weight fragments; the workgroup leaves one XOR word in
+// sink[blockIdx.x] so the loads cannot be dropped.
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, int64_t n16, int64_t span16,
+                                                         uint32_t* __restrict__ sink) {
+  __shared__ uint32_t wx[4];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t begin = (static_cast<int64_t>(blockIdx.x) * 4 + w) * span16;
+  const int64_t end = begin + span16 < n16 ? begin + span16 : n16;
+  uint32_t x = 0;
+  int64_t c = begin + lane;
+  for (; c + (kReadUnroll - 1) * kWave < end; c += kReadUnroll * kWave) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + c + u * kWave);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; c < end; c += kWave) {
+    const u32x4 v = __builtin_nontemporal_load(src + c);
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o, kWave));
+  if (lane == 0) wx[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  // 128 KB per wave, or more so that the grid stays within kReadProbeBlocks workgroups
+  const int64_t min_span = (n16 + 4ll * kReadProbeBlocks - 1) / (4ll * kReadProbeBlocks);
+  const int64_t span16 = min_span > 8192 ? min_span : 8192;
+  const int blocks = static_cast<int>((n16 + 4 * span16 - 1) / (4 * span16));
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(src), n16,
+                     span16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* src, void* dst, int64_t n_mats, int rows, int row_bytes, hipStream_t stream) {
   const int64_t n_chunks = n_mats * rows * (row_bytes / 16);

@@ -84,6 +84,17 @@ def test_layer_forward_parity_packed_weights(name):
     _check_layer(MID[name], seed=2, packed=True)
 
 
+def test_hbm_read_probe_reads_every_byte_once():
+    """The XOR of the probe's checksum words is the XOR of every 32-bit word of the buffer."""
+    rng = np.random.default_rng(4)
+    words = rng.integers(-2 ** 31, 2 ** 31, size=(1 << 18) + 12, dtype=np.int64).astype(np.int32)
+    buf = torch.from_numpy(words).cuda()
+    sink = torch.zeros(moe.HBM_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    moe.moe_hbm_read_probe(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy())
+    assert got == np.bitwise_xor.reduce(words)
+
+
 def test_pack_weights_layout():
     """moe_pack_weights places row (16 f + l % 16), bytes [64 s + 16 (l / 16), +16) at run (f, s), chunk l."""
     rng = np.random.default_rng(3)

@@ -72,6 +72,17 @@ def test_pack_weights_argument_checks():
     assert lib.moe_pack_weights(moe.BF16, -1, 16, 64, fake, fake, None) == moe.ERR_BAD_DIMS
     assert lib.moe_pack_weights(moe.BF16, 1, 16, 64, None, fake, None) == moe.ERR_NULL_ARG
     assert lib.moe_pack_weights(moe.BF16, 0, 16, 64, None, None, None) == moe.OK              # nothing to do
+
+
+def test_hbm_read_probe_argument_checks():
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_hbm_read_probe(fake, 24, fake, None) == moe.ERR_UNSUPPORTED   # not whole 16-byte chunks
+    assert lib.moe_hbm_read_probe(None, 32, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_hbm_read_probe(fake, 32, None, None) == moe.ERR_NULL_ARG
+    assert lib.moe_hbm_read_probe(None, 0, None, None) == moe.OK                  # nothing to read
+
+
 UNSUPPORTED = [dict(D=96), dict(I=100), dict(I_shared=32), dict(E=2048, top_k=2), dict(E=64, top_k=33),
                dict(act="f32", w="bf16"), dict(act="f32", w="f32", out="bf16"), dict(act="bf16", w="f32"),
                dict(act="e4m3", w="e4m3")]
