@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--workload", default="decode_bf16")
     p.add_argument("--layout", default="packed", choices=["packed", "rows"],
                    help="expert weight layout (packed: repacked once by moe_pack_weights before timing)")
-    p.add_argument("--secondary", default="prefill_bf16,skew_prefill_bf16,ep_share_fp8,tiny_fp32",
+    p.add_argument("--secondary", default="prefill_bf16,skew_prefill_bf16,decode_fp8,ep_share_fp8,tiny_fp32",
                    help="comma-separated workloads also measured ('' for none); the bf16 ones reuse the weights")
     p.add_argument("--secondary-steps", type=int, default=20)
     p.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming-read bandwidth probe")

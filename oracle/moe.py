@@ -280,8 +280,8 @@ def quantize_rows_e4m3(a):
     return e4m3_round(scaled.astype(np.float64)), s
 
 
-def layer_from_routing_fp8(x, ids, weights, experts_q, *, expert_begin=0, n_local=None):
-    """One device's fp8 share: e4m3 weights with per-output-channel scales.
+def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_begin=0, n_local=None):
+    """The routed layer with e4m3 expert weights and per-output-channel scales.
 
     ``experts_q[e]`` returns ((g_q, g_s), (u_q, u_s), (d_q, d_s)): codes as
     float64 values on the E4M3 grid ([I, D], [I, D], [D, I]) and fp32
@@ -292,9 +292,13 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, expert_begin=0, n_loca
     3. per expert: g = (x_q W_gq^T) s_x s_g, u likewise, h = silu(g) * u
        in float64;
     4. quantise h per grouped row; out = (h_q W_dq^T) s_h s_d;
-    5. combine with the routing weights (no shared expert: the partial
-       sums go to a reduce-scatter and the shared expert is added once
-       per token by the device that owns it).
+    5. combine with the routing weights, plus the shared expert when
+       ``shared`` = (w_gate, w_up, w_down) is given.  The pages give the
+       routed experts' fp8 storage only; the shared expert keeps the
+       activation precision (its exact float64 image here, unquantised).
+       One device's expert-parallel share passes no shared expert: its
+       partial sums go to a reduce-scatter and the shared expert is added
+       once per token by the device that owns the token.
     """
     x = np.asarray(x, dtype=np.float64)
     if n_local is None:
@@ -318,6 +322,7 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, expert_begin=0, n_loca
         out[s:t] = (hq @ np.asarray(dq, np.float64).T) * hs.astype(np.float64)[:, None] \
             * np.asarray(ds, np.float64)[None, :]
         h_rows[e] = h
-    y = combine(out, weights, inv_pos, None)
+    shared_out = swiglu_expert(x, *shared) if shared is not None else None
+    y = combine(out, weights, inv_pos, shared_out)
     return dict(counts=counts, offsets=offsets, perm_token=perm_token, inv_pos=inv_pos,
-                x_q=xq, x_scale=sx, out_rows=out, y=y)
+                x_q=xq, x_scale=sx, out_rows=out, shared_out=shared_out, y=y)

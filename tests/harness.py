@@ -71,8 +71,9 @@ def oracle_layer(inp: synth.LayerInputs, logits=None, shared: bool = True) -> di
     ids, w = oracle_routing(inp, logits)
     x = synth.f64(inp.x)
     if wl.w == "e4m3":
-        res = oracle.layer_from_routing_fp8(x, ids, w, synth.ExpertViewFP8(inp), expert_begin=wl.expert_begin,
-                                            n_local=wl.local)
+        sh = synth.shared_f64(inp) if shared else None
+        res = oracle.layer_from_routing_fp8(x, ids, w, synth.ExpertViewFP8(inp), shared=sh,
+                                            expert_begin=wl.expert_begin, n_local=wl.local)
     else:
         sh = synth.shared_f64(inp) if shared else None
         res = oracle.layer_from_routing(x, ids, w, synth.ExpertView(inp), shared=sh,

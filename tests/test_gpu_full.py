@@ -123,3 +123,26 @@ def test_ep_share_fp8_full_size():
     # tokens with no local expert get an all-zero partial sum
     none_local = np.nonzero(~((ids >= 0) & (ids < 64)).any(axis=1))[0]
     assert none_local.size > 0 and np.all(g["y"][none_local] == 0)
+
+
+def test_decode_fp8_full_size():
+    """The decode batch with e4m3 routed experts (router and shared expert bf16)."""
+    wl = synth.WORKLOADS["decode_fp8"]
+    inp = synth.make_inputs(wl, 0, "cuda")
+    g = gpu_layer(inp, packed=True)
+    ids, w = oracle.route(g["logits"], wl.top_k, renormalize=wl.renormalize)
+    ids_gpu, w_gpu = oracle.unpack_routing(g["packed"])
+    np.testing.assert_array_equal(ids_gpu, ids)
+    np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
+    counts = _check_grouping(inp, g["packed"])
+    assert counts.sum() == 512 * 10
+    s = _sample_tokens(wl.T, 14)
+    x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
+    wr = synth.f64(inp.w_router)
+    l_ref = oracle.router_logits(x_s, wr).astype(np.float64)
+    assert np.all(np.abs(g["logits"][s] - l_ref) <= logit_bound(x_s, wr, l_ref))
+    ref = oracle.layer_from_routing_fp8(x_s, ids[s], w[s], synth.ExpertViewFP8(inp), shared=synth.shared_f64(inp))
+    err = rel_err(g["y"][s], ref["y"])
+    assert err <= tolerance(wl), f"decode fp8: sampled rel err {err:.3e}"
+    del inp
+    torch.cuda.empty_cache()

@@ -44,6 +44,11 @@ MID = {
                    expert_begin=8, n_local=8, routing_given=True),
     "slice_fp8_f32out": W("slice_fp8_f32out", T=64, D=256, E=16, top_k=3, I=64, I_shared=0, act="bf16", w="e4m3",
                           out="f32", expert_begin=0, n_local=16, routing_given=True),
+    # fp8 routed experts with the router on and a bf16 shared expert (streaming and tile shapes)
+    "fp8_shared": W("fp8_shared", T=200, D=512, E=32, top_k=4, I=128, I_shared=128, act="bf16", w="e4m3",
+                    out="bf16"),
+    "fp8_shared_tile": W("fp8_shared_tile", T=512, D=256, E=16, top_k=4, I=192, I_shared=64, act="bf16",
+                         w="e4m3", out="bf16"),
     # no renormalisation; k = 1
     "norenorm_k1": W("norenorm_k1", T=77, D=128, E=8, top_k=1, I=64, I_shared=64, act="bf16", w="bf16",
                      out="bf16", renormalize=False),
@@ -78,7 +83,8 @@ def test_layer_forward_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "mid_fp32", "decode_like_bf16", "mid_bf16", "mid_bf16_f32out",
-                                  "skew_bf16", "slice_fp8", "slice_fp8_f32out", "one_token"])
+                                  "skew_bf16", "slice_fp8", "slice_fp8_f32out", "fp8_shared", "fp8_shared_tile",
+                                  "one_token"])
 def test_layer_forward_parity_packed_weights(name):
     """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
     _check_layer(MID[name], seed=2, packed=True)

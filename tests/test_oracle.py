@@ -438,6 +438,29 @@ def test_fp8_share_with_single_intermediate_channel_is_exact_layer_on_dequantise
     np.testing.assert_allclose(got["y"], ref["y"], rtol=0, atol=2e-6 * np.abs(ref["y"]).max())
 
 
+def test_fp8_layer_shared_expert_runs_unquantised_on_x_with_weight_one():
+    """The fp8 layer with a shared expert = its routed part (pinned above) + the shared
+    expert of the exact bf16 layer evaluated on the unquantised x.  The shared-only term
+    comes from the exact layer with all routing weights zero, so a shared expert applied
+    to the quantised x, scaled, or dropped fails."""
+    rng = np.random.default_rng(23)
+    T, D, E, k, Is = 24, 32, 6, 2, 16
+    x = numerics.bf16_round(rng.standard_normal((T, D)).astype(np.float32))
+    gq, gs = _fp8_weights(rng, E, 1, D)
+    uq, us = _fp8_weights(rng, E, 1, D)
+    dq, ds = _fp8_weights(rng, E, D, 1)
+    sh = tuple(numerics.bf16_round((rng.standard_normal(shape) / np.sqrt(shape[1])).astype(np.float32))
+               for shape in ((Is, D), (Is, D), (D, Is)))
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    experts_q = [((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])) for e in range(E)]
+    got = oracle.layer_from_routing_fp8(x, ids, w, experts_q, shared=sh)["y"]
+    routed = oracle.layer_from_routing_fp8(x, ids, w, experts_q)["y"]
+    deq = [(gq[e] * gs[e][:, None], uq[e] * us[e][:, None], dq[e] * ds[e][:, None]) for e in range(E)]
+    shared_only = oracle.layer_from_routing(x, ids, np.zeros_like(w), deq, shared=sh)["y"]
+    assert np.abs(shared_only).max() > 0.1
+    np.testing.assert_allclose(got, routed + shared_only, rtol=0, atol=1e-12 * np.abs(got).max())
+
+
 def test_fp8_share_close_to_exact_layer():
     """Quantisation moves y by a few percent at these small widths (each E4M3 operand carries
     up to 2**-4 relative error); a dropped or doubled scale would move it by O(1).  Where
