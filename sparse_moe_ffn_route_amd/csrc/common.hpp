@@ -98,6 +98,19 @@ template <> __device__ __forceinline__ f32x4 mfma_chunk<EL_E4M3>(const u32x4& a,
   return c;
 }
 
+// Two 16-byte E4M3 K-chunks per lane (the chunks of two consecutive 64-byte K slices,
+// A and B alike) through one 16x16x128 MFMA of gfx950's f8f6f4 family: both operands
+// OCP E4M3 (format code 0), block scales 2^0 (E8M0 127).  Which K index each byte
+// stands for does not matter as long as A and B use the same arrangement, which they do.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_e4m3_pair(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                                f32x4 c) {
+  const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers
 // ---------------------------------------------------------------------------

@@ -287,6 +287,38 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
         auto frag_at = [&](int q) {
           return *reinterpret_cast<const u32x4*>(sb + (q % MFR) * 16 * LDS_ROW + (q / MFR) * 64);
         };
+        if constexpr (EL == EL_E4M3 && KSTEPS % 2 == 0) {
+          // E4M3: K slices in pairs through the 16x16x128 MFMA, one fragment's pair ahead;
+          // a lone last slice (odd tail) is paired with zeros on both sides.
+          constexpr int NP = KSTEPS / 2;
+          const int npairs = (nst + 1) / 2;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          u32x4 bl[2], bh[2];
+          auto rd = [&](int q, u32x4& lo, u32x4& hi) {
+            const int sp = q / MFR, mf = q % MFR;
+            lo = frag_at((2 * sp) * MFR + mf);
+            hi = 2 * sp + 1 < nst ? frag_at((2 * sp + 1) * MFR + mf) : z;
+          };
+          rd(0, bl[0], bh[0]);
+#pragma unroll
+          for (int sp = 0; sp < NP; ++sp) {
+            if (sp >= npairs) break;
+            const bool two = 2 * sp + 1 < nst;
+#pragma unroll
+            for (int mf = 0; mf < MFR; ++mf) {
+              const int cur = sp * MFR + mf, nx = cur + 1;
+              if (nx < NP * MFR && nx / MFR < npairs) rd(nx, bl[nx & 1], bh[nx & 1]);
+#pragma unroll
+              for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf)
+                  acc[a][nf][mf] = mfma_e4m3_pair(w[a][nf][2 * sp], two ? w[a][nf][2 * sp + 1] : z, bl[cur & 1],
+                                                  bh[cur & 1], acc[a][nf][mf]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          return;
+        }
         u32x4 bq[NQ];
 #pragma unroll
         for (int q = 0; q < kLdsAhead; ++q)
@@ -448,9 +480,33 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
         }
       }
     };
-    auto compute = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf) {
+    // E4M3: slices s and s + 1 through one 16x16x128 MFMA (two = false: s is a lone last
+    // slice, paired with zeros on both sides)
+    auto step2 = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int s, bool two) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) step(w, buf, s);
+      for (int mf = 0; mf < MF; ++mf) {
+        if (MF == 1 || mf < mf_active) {
+          const uint8_t* bp = &sA[buf][(mf * 16 + lrow) * LDS_ROW + s * 64 + lgrp * 16];
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+          const u32x4 b1 = two ? *reinterpret_cast<const u32x4*>(bp + 64) : z;
+#pragma unroll
+          for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+              acc[a][nf][mf] = mfma_e4m3_pair(w[a][nf][s], two ? w[a][nf][s + 1] : z, b0, b1, acc[a][nf][mf]);
+        }
+      }
+    };
+    constexpr bool kPairs = EL == EL_E4M3 && KSTEPS % 2 == 0;
+    auto compute = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf) {
+      if constexpr (kPairs) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s += 2) step2(w, buf, s, true);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) step(w, buf, s);
+      }
     };
 
     // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
@@ -490,9 +546,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
           for (int nf = 0; nf < NF; ++nf)
             if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * SSTEP);
       __syncthreads();
+      if constexpr (kPairs) {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        if (s < tail_steps) step(wb[0], buf, s);
+        for (int s = 0; s < KSTEPS; s += 2)
+          if (s < tail_steps) step2(wb[0], buf, s, s + 1 < tail_steps);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          if (s < tail_steps) step(wb[0], buf, s);
+      }
     }
     epilogue(acc);
   }
