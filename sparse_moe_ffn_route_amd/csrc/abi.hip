@@ -45,18 +45,31 @@ int check_dims(const moe_dims* d) {
 
 // Shape of the router projection: 32-row streaming tiles (E / 128 N-tiles per 32 tokens
 // already fill the chip at prefill sizes; small T is split along D instead).
-int router_shape(const moe_dims&) { return kShapeStream32; }
+// Router projection shape: 256-row tiles once there are enough tokens for each W_r byte
+// to feed 256 of them (and x fits the tile shape's 32-bit offsets); 32-row streaming
+// tiles below that.
+int router_shape(const moe_dims& d) {
+  const int64_t x_bytes = static_cast<int64_t>(d.T) * d.D * act_size(d.act_dtype);
+  return d.T >= 2048 && x_bytes < (1ll << 31) ? kShapeTile256 : kShapeStream32;
+}
 
-// K splits of the router projection: enough workgroups to cover the chip when T is
-// small (decode), none when the M x N tiles already do (prefill).
+// K splits of the router projection (partial sums added in order by the route kernel):
+// enough workgroups to cover the chip, at most 512 tiles in the streaming shape and
+// at least 256 (with at most 4 partial products) in the tile shape.
 int router_splits(const moe_dims& d) {
+  const int shape = router_shape(d);
   const int row_bytes = d.D * act_size(d.act_dtype);
-  if (row_bytes % 512) return 1;
-  const int blocks = row_bytes / 512;
-  const int bm = gemm_bm(router_shape(d)), bn = gemm_bn(false, router_shape(d));
-  const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn);
+  const int kblk = shape == kShapeTile256 ? 128 : 512;  // bytes per K block of the shape
+  if (row_bytes % kblk) return 1;
+  const int blocks = row_bytes / kblk;
+  const int bm = gemm_bm(shape), bn = gemm_bn(false, shape);
+  const int64_t tiles = static_cast<int64_t>((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn);
   int s = 1;
-  while (s * 2 <= blocks && blocks % (s * 2) == 0 && static_cast<int64_t>(tiles) * s * 2 <= 512) s *= 2;
+  if (shape == kShapeTile256) {
+    while (s < 4 && tiles * s < 256 && s * 2 <= blocks && blocks % (s * 2) == 0) s *= 2;
+  } else {
+    while (s * 2 <= blocks && blocks % (s * 2) == 0 && tiles * s * 2 <= 512) s *= 2;
+  }
   return s;
 }
 

@@ -183,10 +183,11 @@ def test_route_from_given_logits(T, E, k, kind, renorm):
 
 
 @pytest.mark.parametrize("split", [False, True])
-def test_route_with_router_projection_bf16(split):
-    """Without scratch the projection is one pass over D; with it, small T splits D into
-    partial products summed in a fixed order by the routing kernel."""
-    T, D, E, k = 333, 512, 128, 6
+@pytest.mark.parametrize("T,D,E,k", [(333, 512, 128, 6), (3000, 512, 200, 8)])
+def test_route_with_router_projection_bf16(split, T, D, E, k):
+    """Without scratch the projection is one pass over D; with it, D is split into
+    partial products summed in a fixed order by the routing kernel.  333 tokens take the
+    32-row streaming tiles, 3000 the 256-row tiles (ragged last tile, E below one N-tile)."""
     rng = np.random.default_rng(1)
     x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
     wr = torch.from_numpy((rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)).to(torch.bfloat16)
