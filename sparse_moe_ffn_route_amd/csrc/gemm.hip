@@ -566,23 +566,27 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 // NT: non-temporal weight loads, used where each weight byte is read by one tile and
 // the loads cover whole contiguous runs (packed layout); with row-major weights a
 // 128-byte line is split over two load instructions, and the hint costs bandwidth.
-template <int SHAPE, bool SWIGLU, bool PACKED> struct Shape;
-template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream16, SWIGLU, PACKED> {
-  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, NBUF = 2, MINB = 2, TDEPTH = 1;
+// stream16 with 16-bit weights: one workgroup per CU and a four-block weight ring
+// (three blocks in flight per wave) keeps more bytes in flight than two workgroups with
+// a two-block ring; with E4M3 weights two workgroups per CU measured faster.
+template <int EL, int SHAPE, bool SWIGLU, bool PACKED> struct Shape;
+template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream16, SWIGLU, PACKED> {
+  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, TDEPTH = 1;
+  static constexpr int NBUF = EL == EL_E4M3 ? 2 : 4, MINB = EL == EL_E4M3 ? 2 : 1;
   static constexpr bool NT = PACKED;
 };
-template <bool SWIGLU, bool PACKED> struct Shape<kShapeStream32, SWIGLU, PACKED> {
+template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream32, SWIGLU, PACKED> {
   static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2, TDEPTH = 1;
   static constexpr bool NT = PACKED;
 };
-template <bool SWIGLU, bool PACKED> struct Shape<kShapeTile256, SWIGLU, PACKED> {
+template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIGLU, PACKED> {
   static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1, TDEPTH = 2;
   static constexpr bool NT = PACKED;
 };
 
 template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
 hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
-  using S = Shape<SHAPE, SWIGLU, PACKED>;
+  using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
   constexpr int NF = gemm_nf(SWIGLU, SHAPE);
   constexpr int BM = 16 * S::MF, BN = 4 * NF * 16;
   int tiles1 = 0;
