@@ -40,7 +40,7 @@ __device__ __forceinline__ void store8(void* base, size_t idx, const float v[8])
   if (OUT == EL_BF16) {
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = f32_to_bf16_bits(v[2 * q]) | (f32_to_bf16_bits(v[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) w[q] = bf16x2_bits(v[2 * q], v[2 * q + 1]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);

@@ -26,13 +26,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float -> bfloat16 bits, round to nearest even (finite inputs; infinities stay infinite).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // Two floats -> two OCP E4M3 codes in the low 16 bits (hardware convert, nearest even).
 // Callers clamp to +-448 first, so the convert never sees an out-of-range value.
 __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
@@ -60,7 +53,16 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// Two floats -> two bfloat16 (low half = a), round to nearest even; one gfx950 convert.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp):
+// for z -> -inf the reciprocal of +inf is 0 and the result is -0, for z -> +inf it is z.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------
 // One 16-byte K-chunk per lane through the 16x16 MFMA family.

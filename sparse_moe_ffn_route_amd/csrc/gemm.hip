@@ -59,12 +59,11 @@ template <> struct OutStore<EL_F32> {
 template <> struct OutStore<EL_BF16> {
   static __device__ __forceinline__ void store4(void* base, size_t idx, const float v[4], int valid) {
     uint16_t* p = static_cast<uint16_t*>(base) + idx;
-    const uint32_t b0 = f32_to_bf16_bits(v[0]), b1 = f32_to_bf16_bits(v[1]);
-    const uint32_t b2 = f32_to_bf16_bits(v[2]), b3 = f32_to_bf16_bits(v[3]);
+    const uint32_t b01 = bf16x2_bits(v[0], v[1]), b23 = bf16x2_bits(v[2], v[3]);
     if (valid >= 4 && (idx & 3) == 0) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      *reinterpret_cast<uint2*>(p) = make_uint2(b01, b23);
     } else {
-      const uint32_t b[4] = {b0, b1, b2, b3};
+      const uint32_t b[4] = {b01 & 0xFFFFu, b01 >> 16, b23 & 0xFFFFu, b23 >> 16};
       for (int r = 0; r < (valid < 4 ? valid : 4); ++r) p[r] = static_cast<uint16_t>(b[r]);
     }
   }
