@@ -44,9 +44,10 @@ def parse():
     p.add_argument("--workload", default="decode_bf16")
     p.add_argument("--layout", default="packed", choices=["packed", "rows"],
                    help="expert weight layout (packed: repacked once by moe_pack_weights before timing)")
-    p.add_argument("--secondary", default="prefill_bf16,skew_prefill_bf16,decode_fp8,ep_share_fp8,tiny_fp32",
+    p.add_argument("--secondary",
+                   default="prefill_bf16,skew_prefill_bf16,prefill32k_bf16,decode_fp8,ep_share_fp8,tiny_fp32",
                    help="comma-separated workloads also measured ('' for none); the bf16 ones reuse the weights")
-    p.add_argument("--secondary-steps", type=int, default=20)
+    p.add_argument("--secondary-steps", type=int, default=50)
     p.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming-read bandwidth probe")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens of the oracle sample (0: whole batch)")

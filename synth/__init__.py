@@ -98,6 +98,10 @@ WORKLOADS = {
     "ep_share_fp8": Workload("ep_share_fp8", T=8192, D=4096, E=512, top_k=10, I=1024, I_shared=0,
                              act="bf16", w="e4m3", out="bf16", expert_begin=0, n_local=64,
                              routing_given=True),
+    # A 32K-token prefill chunk (~640 rows per expert): large enough for the grouped GEMMs
+    # to be MFMA-bound rather than weight-stream bound; a supplementary probe.
+    "prefill32k_bf16": Workload("prefill32k_bf16", T=32768, D=4096, E=512, top_k=10, I=1024, I_shared=1024,
+                                act="bf16", w="bf16", out="bf16"),
     # The decode batch with the routed experts stored as e4m3 codes + per-channel fp32 scales
     # (about one byte per parameter); router and shared expert stay bf16.
     "decode_fp8": Workload("decode_fp8", T=512, D=4096, E=512, top_k=10, I=1024, I_shared=1024,

@@ -99,6 +99,19 @@ def test_prefill_full_size(big_layer):
     assert counts.sum() == 8192 * 10
 
 
+def test_prefill32k_full_size(big_layer):
+    """The 32K-token probe: experts of ~640 rows span three 256-row M-tiles."""
+    wl = synth.WORKLOADS["prefill32k_bf16"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(32768)
+    x = torch.randn(wl.T, wl.D, generator=gen, device="cuda").to(torch.bfloat16)
+    b = big_layer
+    inp = synth.LayerInputs(wl, x, b.w_router, b.w_gate, b.w_up, b.w_down, None, None, None, b.ws_gate, b.ws_up,
+                            b.ws_down, None, None)
+    counts = _check_routed_layer(inp, 15)
+    assert counts.sum() == 32768 * 10 and counts.min() > 256
+
+
 def test_skewed_prefill_full_size(big_layer):
     counts = _check_routed_layer(_variant(big_layer, "skew_prefill_bf16"), 12)
     assert (counts == 0).sum() == 32                      # the never-chosen experts stay empty
@@ -144,5 +157,23 @@ def test_decode_fp8_full_size():
     ref = oracle.layer_from_routing_fp8(x_s, ids[s], w[s], synth.ExpertViewFP8(inp), shared=synth.shared_f64(inp))
     err = rel_err(g["y"][s], ref["y"])
     assert err <= tolerance(wl), f"decode fp8: sampled rel err {err:.3e}"
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_operands_past_2gib_take_the_streaming_shape():
+    """65536 tokens x top-8 x I = 1024 puts the grouped h rows past 2 GiB (fp32 bound): the
+    grouped GEMMs fall back from the 256-row tile shape to the 32-row streaming shape."""
+    wl = synth.Workload("big_rows", T=65536, D=256, E=64, top_k=8, I=1024, I_shared=0, act="bf16", w="bf16",
+                        out="bf16")
+    inp = synth.make_inputs(wl, 0, "cuda")
+    g = gpu_layer(inp, packed=True)
+    ids, w = oracle.route(g["logits"], wl.top_k)
+    np.testing.assert_array_equal(oracle.unpack_routing(g["packed"])[0], ids)
+    s = _sample_tokens(wl.T, 16)
+    x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
+    ref = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp))
+    err = rel_err(g["y"][s], ref["y"])
+    assert err <= tolerance(wl), f"past-2GiB batch: sampled rel err {err:.3e}"
     del inp
     torch.cuda.empty_cache()
