@@ -242,6 +242,31 @@ def copy_probe(mib):
     return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}
 
 
+def router_variants(wl, x, w_router, reps=20):
+    """moe_route (projection GEMM + route kernel) against moe_route_fused on the same x, in microseconds."""
+    import torch
+    import sparse_moe_ffn_route_amd as moe
+    T = x.shape[0]
+    d = moe.make_dims(T, wl.D, wl.E, wl.top_k, wl.I, wl.I_shared, 0, wl.E, wl.renormalize, wl.act, wl.w, wl.out)
+    ws = moe.workspace(d)
+    logits = torch.empty(T, wl.E, dtype=torch.float32, device="cuda")
+    packed = torch.empty(T, 2, wl.top_k, dtype=torch.int32, device="cuda")
+    calls = {"two_kernel_us": lambda: moe.moe_route(d, x, w_router, logits, None, packed, ws=ws),
+             "fused_us": lambda: moe.moe_route_fused(d, x, w_router, None, None, packed)}
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps * 1e3, 1)
+    return out
+
+
 def hbm_probe(buf, reps=5):
     """Best-of-reps streaming-read bandwidth (GB/s) of moe_hbm_read_probe over buf."""
     import torch
@@ -321,6 +346,16 @@ def main():
         del layer2, inp2, pw2
         torch.cuda.empty_cache()
 
+    routers = None
+    if wl.E <= 512 and not wl.routing_given:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(synth._torch_seed(0, "x", 1))
+        x8k = (torch.randn(8192, wl.D, generator=g, device="cuda")).to(torch.bfloat16)
+        routers = {f"T={inp.x.shape[0]}": router_variants(wl, inp.x, inp.w_router),
+                   "T=8192": router_variants(wl, x8k, inp.w_router)}
+        del x8k
+        print(f"[bench] router variants: {routers}", file=sys.stderr, flush=True)
+
     measured = None
     if not args.no_hbm_probe:
         measured = {"hbm_read_GBs": hbm_probe(packed_w["w_gate"] if packed_w else inp.w_gate),
@@ -359,6 +394,8 @@ def main():
         "secondary": secondary,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if routers:
+        out["router_variants"] = routers
     if measured:
         out["measured_peaks"] = measured
         out["roofline"]["frac_of_measured_hbm"] = round(out["roofline"]["achieved"] / measured["hbm_read_GBs"], 4)

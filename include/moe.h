@@ -135,6 +135,23 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* 
               const float* logit_bias, int32_t* packed, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same routing as moe_route with x and w_router given, computed by one fused kernel:
+ * the projection, the top-k selection, the weights and the packed blob per block of 64
+ * tokens, so the fp32 logits stay on chip unless `logits` asks for a copy.  Fusing the
+ * selection into the kernel that produces the logits is the open item of Playbook
+ * "The Remaining Roadmap".  Opt-in: every workgroup streams all of w_router, which on
+ * MI355X is slower than moe_route's projection spread over the whole chip.
+ *
+ *   x, w_router, logit_bias, packed   as for moe_route (x and w_router required)
+ *   logits     [T][E] fp32 output copy of the logits, or NULL for none
+ * Needs E <= 512 and x, w_router each below 2 GiB, else MOE_ERR_UNSUPPORTED.  The ids
+ * and weights equal moe_route's for the same fp32 logits; the logits themselves may
+ * differ by summation order (both within the fp32 accumulation bound).  No workspace.
+ */
+int moe_route_fused(const moe_dims* dims, const void* x, const void* w_router, float* logits,
+                    const float* logit_bias, int32_t* packed, void* stream);
+
+/*
  * Permutation: group the (token, slot) pairs whose expert is local by expert
  * (experts ascending, (t, j) ascending inside an expert).  Ids outside the local
  * slice (other devices' experts, or any value outside [0, E)) are skipped.

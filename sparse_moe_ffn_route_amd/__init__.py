@@ -33,8 +33,8 @@ OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1,
 
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
-    "moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine",
-    "moe_layer_forward", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
+    "moe_workspace_bytes", "moe_route", "moe_route_fused", "moe_permute", "moe_grouped_ffn",
+    "moe_unpermute_combine", "moe_layer_forward", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
     "moe_abi_version",
 )
 
@@ -73,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
+    lib.moe_route_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_fused.restype = i32
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
     lib.moe_grouped_ffn.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -141,14 +143,48 @@ def workspace(dims: moe_dims, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+_ELEM_BYTES = {F32: 4, BF16: 2, E4M3: 1}
+
+
+def _need(t: Optional[torch.Tensor], nbytes: int, what: str):
+    """Refuse a tensor smaller than the dims say (the kernels trust the dims)."""
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, the dims need {nbytes}")
+
+
+def _check_io(dims, x=None, logits=None, packed=None, bias=None, y=None, w_router=None):
+    T, D, E, k = dims.T, dims.D, dims.E, dims.top_k
+    _need(x, T * D * _ELEM_BYTES[dims.act_dtype], "x")
+    _need(w_router, E * D * _ELEM_BYTES[dims.act_dtype], "w_router")
+    _need(logits, T * E * 4, "logits")
+    _need(packed, T * 2 * k * 4, "packed routing")
+    _need(bias, E * 4, "logit bias")
+    _need(y, T * D * _ELEM_BYTES[dims.out_dtype], "y")
+
+
 def moe_route(dims, x, w_router, logits, logit_bias, packed, ws=None, stream=None):
+    _check_io(dims, x=x, logits=logits, packed=packed, bias=logit_bias, w_router=w_router)
     _check(library().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(logit_bias),
                                _ptr(packed), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_route")
 
 
+def moe_route_fused(dims, x, w_router, logits, logit_bias, packed, stream=None):
+    """Fused projection + top-k + blob (logits: optional fp32 copy, or None)."""
+    _check_io(dims, x=x, logits=logits, packed=packed, bias=logit_bias, w_router=w_router)
+    _check(library().moe_route_fused(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(logit_bias),
+                                     _ptr(packed), _stream(stream)), "moe_route_fused")
+
+
 def moe_permute(dims, packed, counts, offsets, perm_token, inv_pos, x=None, x_perm=None, x_perm_scale=None,
                 ws=None, stream=None):
+    tk = dims.T * dims.top_k
+    _check_io(dims, x=x, packed=packed)
+    _need(counts, dims.n_local * 4, "counts")
+    _need(offsets, (dims.n_local + 1) * 4, "offsets")
+    _need(perm_token, tk * 4, "perm_token")
+    _need(inv_pos, tk * 4, "inv_pos")
+    _need(x_perm, tk * dims.D * (1 if dims.w_dtype == E4M3 else _ELEM_BYTES[dims.act_dtype]), "x_perm")
     _check(library().moe_permute(ctypes.byref(dims), _ptr(packed), _ptr(counts), _ptr(offsets), _ptr(perm_token),
                                  _ptr(inv_pos), _ptr(x), _ptr(x_perm), _ptr(x_perm_scale), _ptr(ws),
                                  ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
@@ -163,6 +199,9 @@ def moe_grouped_ffn(dims, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_
 
 
 def moe_unpermute_combine(dims, out_rows, packed, inv_pos, shared_out, y, stream=None):
+    _check_io(dims, packed=packed, y=y)
+    _need(inv_pos, dims.T * dims.top_k * 4, "inv_pos")
+    _need(shared_out, dims.T * dims.D * _ELEM_BYTES[dims.out_dtype], "shared_out")
     _check(library().moe_unpermute_combine(ctypes.byref(dims), _ptr(out_rows), _ptr(packed), _ptr(inv_pos),
                                            _ptr(shared_out), _ptr(y), _stream(stream)), "moe_unpermute_combine")
 
@@ -186,6 +225,8 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
         if len(stage_events) != STAGE_EVENTS:
             raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
         ev = (ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
+    _check_io(dims, x=x, logits=logits_out, packed=packed_in, bias=logit_bias, y=y)
+    _need(packed_out, dims.T * 2 * dims.top_k * 4, "packed_out")
     _check(library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _ptr(packed_in),
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, ev, _stream(stream)),

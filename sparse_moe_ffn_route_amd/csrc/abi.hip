@@ -163,6 +163,16 @@ GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, in
   return p;
 }
 
+// The fused router kernel (projection, top-k and blob in one launch) serves E <= 512
+// when x and W_r fit its 32-bit offsets.  It is an opt-in entry point: each 64-token
+// workgroup streams all of W_r, which measured slower on MI355X than the GEMM split
+// over the whole chip followed by the route kernel.
+bool fused_router_fits(const moe_dims& d) {
+  const int64_t es = act_size(d.act_dtype);
+  return d.E <= kMaxFusedExperts && static_cast<int64_t>(d.T) * d.D * es < (1ll << 31) &&
+         static_cast<int64_t>(d.E) * d.D * es < (1ll << 31);
+}
+
 // Router projection + top-k.  parts: scratch for split-K partial products (NULL: no split).
 int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* logits, float* parts,
                  const float* bias, int32_t* packed, hipStream_t s) {
@@ -274,6 +284,18 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* 
   if (d.T == 0) return MOE_OK;
   return route_tokens(d, x, w_router, logits, ws ? at<float>(ws, L.logits_part) : nullptr, logit_bias, packed,
                       static_cast<hipStream_t>(stream));
+}
+
+int moe_route_fused(const moe_dims* dims, const void* x, const void* w_router, float* logits, const float* logit_bias,
+                    int32_t* packed, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (!x || !w_router || !packed) return MOE_ERR_NULL_ARG;
+  if (!fused_router_fits(d)) return MOE_ERR_UNSUPPORTED;
+  if (d.T == 0) return MOE_OK;
+  return hip_status(launch_router_topk(d.act_dtype, x, w_router, logit_bias, d.T, d.D, d.E, d.top_k, d.renormalize,
+                                       logits, packed, static_cast<hipStream_t>(stream)));
 }
 
 int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, int32_t* offsets, int32_t* perm_token,

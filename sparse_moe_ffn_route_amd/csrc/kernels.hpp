@@ -51,6 +51,12 @@ constexpr int gemm_nf(bool swiglu, int shape) {
 // Output channels per workgroup (4 waves).
 constexpr int gemm_bn(bool swiglu, int shape) { return 4 * gemm_nf(swiglu, shape) * 16; }
 
+// Fused router projection + top-k for E <= kMaxFusedExperts (act: bf16 or fp32 codes of
+// EL_*): 64 tokens per workgroup; logits_out (nullable) receives the fp32 logits.
+constexpr int kMaxFusedExperts = 512;
+hipError_t launch_router_topk(int el, const void* x, const void* w_router, const float* bias, int T, int D, int E,
+                              int k, int renormalize, float* logits_out, int32_t* packed, hipStream_t stream);
+
 // Top-k routing.  When n_parts > 1, the logits are the sum of n_parts partial products
 // parts[p][T][E] (added in order p = 0, 1, ...), written to `logits` before routing.
 hipError_t launch_route(const float* parts, int n_parts, float* logits, const float* bias, int T, int E, int k,

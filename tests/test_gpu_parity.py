@@ -205,6 +205,37 @@ def test_route_with_router_projection_bf16(split, T, D, E, k):
     np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("T,D,E,k,act,renorm,biased", [
+    (333, 512, 128, 6, "bf16", True, False),     # ragged last 64-token block, E below 512
+    (3000, 512, 200, 8, "bf16", True, True),     # bias, E not a multiple of 64
+    (100, 256, 64, 4, "f32", False, False),      # fp32 operands, no renormalisation
+    (512, 4096, 512, 10, "bf16", True, False),   # the decode router shape
+])
+def test_route_fused_matches_definition(T, D, E, k, act, renorm, biased):
+    """The fused router: logits within the fp32 bound, routing bit-exact from its own logits,
+    and the same blob whether or not the logits are copied out."""
+    rng = np.random.default_rng(T + E)
+    dt = torch.float32 if act == "f32" else torch.bfloat16
+    x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(dt)
+    wr = torch.from_numpy((rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)).to(dt)
+    bias = torch.from_numpy(rng.standard_normal(E).astype(np.float32) * 0.5) if biased else None
+    d = moe.make_dims(T, D, E, k, 64, act=act, w=act, out=act, renormalize=renorm)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    packed = torch.empty(T, 2, k, dtype=torch.int32, device="cuda")
+    moe.moe_route_fused(d, x.cuda(), wr.cuda(), logits, None if bias is None else bias.cuda(), packed)
+    x64, w64 = to_np(x), to_np(wr)
+    l_ref = oracle.router_logits(x64, w64).astype(np.float64)
+    lg = logits.cpu().numpy()
+    assert np.all(np.abs(lg - l_ref) <= logit_bound(x64, w64, l_ref))
+    ids, w = oracle.route(lg, k, bias=None if bias is None else bias.numpy(), renormalize=renorm)
+    ids_gpu, w_gpu = oracle.unpack_routing(packed.cpu().numpy())
+    np.testing.assert_array_equal(ids_gpu, ids)
+    np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
+    packed2 = torch.empty_like(packed)
+    moe.moe_route_fused(d, x.cuda(), wr.cuda(), None, None if bias is None else bias.cuda(), packed2)
+    np.testing.assert_array_equal(packed2.cpu().numpy(), packed.cpu().numpy())
+
+
 # ---------------------------------------------------------------------------
 # moe_permute
 # ---------------------------------------------------------------------------

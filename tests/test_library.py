@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import sparse_moe_ffn_route_amd as moe
 import synth
@@ -157,3 +158,32 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.moe_status_string(code)
     assert lib.moe_last_hip_error() == 0
+
+
+def test_binding_refuses_tensors_smaller_than_the_dims():
+    """The kernels trust the dims: a hidden-state tensor with fewer rows than T must be refused before
+    any launch (a 32768-token layer handed 8192 rows would read past the end of x)."""
+    d = moe.make_dims(32768, 256, 16, 2, 64)
+    x_short = torch.zeros(8192, 256, dtype=torch.bfloat16)
+    y = torch.zeros(32768, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="x:"):
+        moe.moe_layer_forward(d, moe.make_weights(), x_short, None, None, y)
+    with pytest.raises(ValueError, match="logits"):
+        moe.moe_route(d, None, None, torch.zeros(10, dtype=torch.float32), None,
+                      torch.zeros(32768 * 4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="perm_token"):
+        moe.moe_permute(d, torch.zeros(32768 * 4, dtype=torch.int32), torch.zeros(16, dtype=torch.int32),
+                        torch.zeros(17, dtype=torch.int32), torch.zeros(5, dtype=torch.int32),
+                        torch.zeros(32768 * 2, dtype=torch.int32))
+
+
+def test_fused_router_argument_checks():
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    big_e = moe.make_dims(64, 256, 1024, 4, 64)
+    assert lib.moe_route_fused(ctypes.byref(big_e), fake, fake, None, None, fake, None) == moe.ERR_UNSUPPORTED
+    d = moe.make_dims(64, 256, 16, 4, 64)
+    assert lib.moe_route_fused(ctypes.byref(d), None, fake, None, None, fake, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, None, None) == moe.ERR_NULL_ARG
+    zero = moe.make_dims(0, 256, 16, 4, 64)
+    assert lib.moe_route_fused(ctypes.byref(zero), fake, fake, None, None, fake, None) == moe.OK
