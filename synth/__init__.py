@@ -150,11 +150,12 @@ def _store(z: "torch.Tensor", dt: str) -> "torch.Tensor":
     return z if dt == "f32" else z.to(_TORCH_DT[dt])
 
 
-def _fp8_channels(z: "torch.Tensor", std: float):
-    """float32 draws [out, in] -> (E4M3 codes [out, in], fp32 scale per output channel [out])."""
+def _fp8_channels(z: "torch.Tensor"):
+    """float32 draws [out, in] (already scaled by the weight std) -> (E4M3 codes [out, in], fp32 scale
+    per output channel [out]), so that codes * scale ~ z: each channel's largest magnitude maps to 448."""
     amax = z.abs().amax(dim=1, keepdim=True).clamp_min(1e-30)
     codes = (z * (448.0 / amax)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-    scale = (amax[:, 0] / 448.0 * std).to(torch.float32)
+    scale = (amax[:, 0] / 448.0).to(torch.float32)
     return codes, scale
 
 
@@ -226,7 +227,7 @@ def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu") -> LayerInputs
         if wl.w == "e4m3":
             codes, scales = [], []
             for e in range(nl):
-                c, s = _fp8_channels(normal(tensor, wl.expert_begin + e, shape, std), std)
+                c, s = _fp8_channels(normal(tensor, wl.expert_begin + e, shape, std))
                 codes.append(c)
                 scales.append(s)
             return torch.stack(codes), torch.stack(scales)
