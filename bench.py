@@ -242,6 +242,24 @@ def copy_probe(mib):
     return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}
 
 
+def audit_of(layer, n_sample=16):
+    """moe_audit of the last step's output on n_sample evenly spaced tokens: fp32 shadow vs the layer."""
+    import torch
+    import sparse_moe_ffn_route_amd as moe
+    T = layer.wl.T
+    sample = torch.linspace(0, T - 1, n_sample, device="cuda").to(torch.int32)
+    layer.step()                                  # y and the routing blob of one call
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    res = moe.moe_audit(layer.dims, layer.weights, layer.inp.x, layer.inp.packed if layer.wl.routing_given
+                        else layer.packed, layer.y, sample)
+    e1.record()
+    torch.cuda.synchronize()
+    r = res.cpu().tolist()
+    return {"samples": n_sample, "max_abs_err": r[0], "max_abs_ref": r[1], "rel_err": r[0] / r[1] if r[1] else None,
+            "ms": round(e0.elapsed_time(e1), 3)}
+
+
 def router_variants(wl, x, w_router, reps=20):
     """moe_route (projection GEMM + route kernel) against moe_route_fused on the same x, in microseconds."""
     import torch
@@ -341,6 +359,8 @@ def main():
         wall2, stages2 = layer2.run(args.secondary_steps, 2)
         sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
         sec["roofline"] = roofline_of(layer2, stages2)
+        if wl2.w == "e4m3":
+            sec["audit"] = audit_of(layer2)
         secondary.append(sec)
         print(f"[bench] {wl2.name}: {sec['ms_per_step']:.3f} ms/step, stages {stages2}", file=sys.stderr, flush=True)
         del layer2, inp2, pw2
@@ -394,6 +414,7 @@ def main():
         "secondary": secondary,
         "kernel_source_hash": kernel_source_hash(),
     }
+    out["audit"] = audit_of(layer)
     if routers:
         out["router_variants"] = routers
     if measured:

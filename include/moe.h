@@ -253,6 +253,35 @@ int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, 
                      void* stream);
 
 /*
+ * Numerical audit: an fp32 shadow of the layer on sampled tokens, compared with the
+ * layer's output.  For each sampled token t the reference is
+ *   ref[t] = sum_j w[t][j] * W_down (silu(W_gate x_t) * (W_up x_t)) over the local slots
+ *            of `packed`, in slot order, + the shared expert (weight 1) if present,
+ * evaluated in fp32 from the stored tensors: E4M3 weights decoded and scaled per channel,
+ * x and h never quantised, SwiGLU with an IEEE division.  It measures what the fast
+ * path's bf16 rounding and fp8 quantisation cost, as the "Numerical Verification Layer"
+ * of Playbook "Roofline Validation" checks low-precision results against a
+ * high-precision evaluation.
+ *
+ *   dims, weights  as for moe_layer_forward (same layout, local slice and dtypes)
+ *   x         [T][D] act_dtype: the hidden states the layer was run on
+ *   packed    [T][2][top_k] int32: the routing the layer used (e.g. its packed_out)
+ *   y         [T][D] out_dtype: the layer's output to audit
+ *   sample    [n_sample] int32 device token indices in [0, T) (clamped into range)
+ *   n_sample  1 .. 4096
+ *   ref_out   [n_sample][D] fp32 output copy of the reference rows, or NULL
+ *   result    [2] fp32 device output: max |y - ref| and max |ref| over the samples
+ *   ws        scratch of ws_bytes >= moe_audit_workspace_bytes(dims, n_sample)
+ * Limits: D, I, I_shared <= 16384 (MOE_ERR_UNSUPPORTED).  T = 0 is MOE_ERR_BAD_DIMS
+ * (nothing to sample).  Not a hot path: it reads every sampled token's expert weights
+ * once per token.
+ */
+size_t moe_audit_workspace_bytes(const moe_dims* dims, int32_t n_sample);
+int moe_audit(const moe_dims* dims, const moe_weights* weights, const void* x, const int32_t* packed,
+              const void* y, const int32_t* sample, int32_t n_sample, float* ref_out, float* result, void* ws,
+              size_t ws_bytes, void* stream);
+
+/*
  * Measurement helper, not part of the layer: reads `bytes` (a multiple of 16) of device
  * memory at buf once with wide non-temporal loads and writes 16384 uint32 words of XOR
  * checksums into sink (device, caller-owned, at least 16384 words).  Timing it over a

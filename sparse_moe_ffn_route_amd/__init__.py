@@ -34,7 +34,7 @@ OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1,
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_route_fused", "moe_permute", "moe_grouped_ffn",
-    "moe_unpermute_combine", "moe_layer_forward", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
+    "moe_unpermute_combine", "moe_layer_forward", "moe_audit_workspace_bytes", "moe_audit", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
     "moe_abi_version",
 )
 
@@ -85,6 +85,10 @@ def library() -> ctypes.CDLL:
     lib.moe_layer_forward.restype = i32
     lib.moe_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_pack_weights.restype = i32
+    lib.moe_audit_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+    lib.moe_audit_workspace_bytes.restype = sz
+    lib.moe_audit.argtypes = [dp, wp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
+    lib.moe_audit.restype = i32
     lib.moe_hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.moe_hbm_read_probe.restype = i32
     lib.moe_status_string.argtypes = [i32]
@@ -231,6 +235,22 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, ev, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_audit(dims, weights: moe_weights, x, packed, y, sample, ref_out=None, stream=None):
+    """fp32 shadow of the layer on the sampled tokens; returns a device tensor [max |y - ref|, max |ref|]."""
+    n = sample.numel()
+    _check_io(dims, x=x, packed=packed, y=y)
+    _need(ref_out, n * dims.D * 4, "ref_out")
+    nbytes = int(library().moe_audit_workspace_bytes(ctypes.byref(dims), n))
+    if nbytes == 0:
+        raise MoeError(ERR_BAD_DIMS, "moe_audit_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    result = torch.empty(2, dtype=torch.float32, device=x.device)
+    _check(library().moe_audit(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _ptr(packed), _ptr(y),
+                               _ptr(sample), n, _ptr(ref_out), _ptr(result), _ptr(ws), nbytes, _stream(stream)),
+           "moe_audit")
+    return result
 
 
 _CODE_OF_TORCH = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3, torch.uint8: E4M3}

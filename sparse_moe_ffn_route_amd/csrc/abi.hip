@@ -428,6 +428,38 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   return hip_status(mark(5));
 }
 
+size_t moe_audit_workspace_bytes(const moe_dims* dims, int32_t n_sample) {
+  if (check_dims(dims) != MOE_OK || n_sample < 1 || n_sample > kAuditMaxSamples) return 0;
+  return audit_workspace_bytes(n_sample, dims->top_k, dims->D, std::max(dims->I, dims->I_shared));
+}
+
+int moe_audit(const moe_dims* dims, const moe_weights* w, const void* x, const int32_t* packed, const void* y,
+              const int32_t* sample, int32_t n_sample, float* ref_out, float* result, void* ws, size_t ws_bytes,
+              void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (n_sample < 1 || n_sample > kAuditMaxSamples) return MOE_ERR_BAD_DIMS;
+  if (d.D > kAuditMaxWidth || d.I > kAuditMaxWidth || d.I_shared > kAuditMaxWidth) return MOE_ERR_UNSUPPORTED;
+  if (!w || !x || !packed || !y || !sample || !result || !ws || !w->w_gate || !w->w_up || !w->w_down)
+    return MOE_ERR_NULL_ARG;
+  if (d.w_dtype == MOE_E4M3 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL_ARG;
+  if (d.I_shared > 0 && w->sh_gate && (!w->sh_up || !w->sh_down)) return MOE_ERR_NULL_ARG;
+  if (d.T == 0) return MOE_ERR_BAD_DIMS;
+  if (ws_bytes < audit_workspace_bytes(n_sample, d.top_k, d.D, std::max(d.I, d.I_shared))) return MOE_ERR_WORKSPACE;
+  AuditLaunch l{};
+  l.x = x; l.packed = packed; l.y = y; l.sample = sample;
+  l.T = d.T; l.D = d.D; l.k = d.top_k; l.I = d.I; l.I_shared = d.I_shared; l.e_begin = d.expert_begin;
+  l.n_local = d.n_local; l.n_sample = n_sample;
+  l.act_el = d.act_dtype == MOE_F32 ? EL_F32 : EL_BF16; l.w_el = w_el(d); l.out_el = d.out_dtype;
+  l.packed_layout = d.weight_layout == MOE_LAYOUT_PACKED;
+  l.w_gate = w->w_gate; l.w_up = w->w_up; l.w_down = w->w_down;
+  l.s_gate = w->s_gate; l.s_up = w->s_up; l.s_down = w->s_down;
+  l.sh_gate = d.I_shared > 0 ? w->sh_gate : nullptr; l.sh_up = w->sh_up; l.sh_down = w->sh_down;
+  l.ref_out = ref_out; l.result = result; l.ws = ws;
+  return hip_status(launch_audit(l, static_cast<hipStream_t>(stream)));
+}
+
 int moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols, const void* src, void* dst,
                      void* stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_E4M3) return MOE_ERR_UNSUPPORTED;

@@ -51,6 +51,32 @@ constexpr int gemm_nf(bool swiglu, int shape) {
 // Output channels per workgroup (4 waves).
 constexpr int gemm_bn(bool swiglu, int shape) { return 4 * gemm_nf(swiglu, shape) * 16; }
 
+// fp32 shadow of the layer on sampled tokens (numerical audit); element types are EL_*.
+struct AuditLaunch {
+  const void* x;
+  const int32_t* packed;
+  const void* y;
+  const int32_t* sample;
+  int T, D, k, I, I_shared, e_begin, n_local, n_sample;
+  int act_el, w_el, out_el, packed_layout;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  const void* sh_gate;
+  const void* sh_up;
+  const void* sh_down;
+  float* ref_out;
+  float* result;
+  void* ws;
+};
+constexpr int kAuditMaxSamples = 4096;
+constexpr int kAuditMaxWidth = 16384;  // D and I limits (one fp32 vector in LDS)
+size_t audit_workspace_bytes(int n_sample, int k, int D, int i_max);
+hipError_t launch_audit(const AuditLaunch& l, hipStream_t stream);
+
 // Fused router projection + top-k for E <= kMaxFusedExperts (act: bf16 or fp32 codes of
 // EL_*): 64 tokens per workgroup; logits_out (nullable) receives the fp32 logits.
 constexpr int kMaxFusedExperts = 512;

@@ -14,6 +14,7 @@ import torch
 import oracle
 import sparse_moe_ffn_route_amd as moe
 import synth
+import harness
 from harness import dims_of, gpu_layer, logit_bound, oracle_layer, oracle_routing, rel_err, to_np, tolerance
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +89,55 @@ def test_layer_forward_parity(name):
 def test_layer_forward_parity_packed_weights(name):
     """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
     _check_layer(MID[name], seed=2, packed=True)
+
+
+class _DequantView:
+    """experts[e] -> dequantised (w_gate, w_up, w_down) in float64: E4M3 codes times their channel scales."""
+
+    def __init__(self, inp):
+        self.q = synth.ExpertViewFP8(inp)
+
+    def __len__(self):
+        return len(self.q)
+
+    def __getitem__(self, e):
+        (gq, gs), (uq, us), (dq, ds) = self.q[e]
+        return gq * gs[:, None], uq * us[:, None], dq * ds[:, None]
+
+
+@pytest.mark.parametrize("name,packed", [("mid_bf16", False), ("mid_bf16", True), ("tiny_fp32", False),
+                                         ("fp8_shared", False), ("fp8_shared", True), ("slice_fp8", True)])
+def test_audit_shadow_is_the_exact_layer(name, packed):
+    """moe_audit's reference rows are the exact layer (stored weights, unquantised x and h) on the
+    sampled tokens with the routing the layer used; its result is max |y - ref| and max |ref|."""
+    wl = MID[name]
+    inp = synth.make_inputs(wl, 4, "cpu")
+    g = gpu_layer(inp, packed=packed)
+    dev = g["dev"]
+    use_shared = wl.I_shared > 0
+    pw = harness.packed_weights(dev) if packed else {n: getattr(dev, n) for n in
+                                                      ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    w = moe.make_weights(dev.w_router, pw["w_gate"], pw["w_up"], pw["w_down"], dev.s_gate, dev.s_up, dev.s_down,
+                         pw["ws_gate"] if use_shared else None, pw["ws_up"] if use_shared else None,
+                         pw["ws_down"] if use_shared else None)
+    d = dims_of(wl, True, packed)
+    rows = np.array(sorted({0, 1, wl.T // 2, wl.T - 1}), dtype=np.int32)
+    sample = torch.from_numpy(rows).cuda()
+    out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
+    y_dev = torch.from_numpy(g["y"]).to(out_dt).cuda()          # exact: the values came from this dtype
+    ref_out = torch.empty(len(rows), wl.D, dtype=torch.float32, device="cuda")
+    res = moe.moe_audit(d, w, dev.x, torch.from_numpy(g["packed"]).cuda(), y_dev, sample, ref_out).cpu().numpy()
+    ref = ref_out.cpu().numpy().astype(np.float64)
+    ids, wts = oracle.unpack_routing(g["packed"])
+    experts = _DequantView(inp) if wl.w == "e4m3" else synth.ExpertView(inp)
+    exact = oracle.layer_from_routing(synth.f64(inp.x)[rows], ids[rows], wts[rows].astype(np.float64), experts,
+                                      shared=synth.shared_f64(inp) if use_shared else None,
+                                      expert_begin=wl.expert_begin, n_local=wl.local)["y"]
+    assert rel_err(ref, exact) <= 1e-4                          # an fp32 evaluation of the exact layer
+    np.testing.assert_allclose(res[1], np.abs(ref).max(), rtol=1e-6)
+    np.testing.assert_allclose(res[0], np.abs(g["y"][rows] - ref).max(), rtol=1e-5, atol=1e-7)
+    bound = 0.1 if wl.w == "e4m3" else tolerance(wl)            # fp8 quantisation shows, a few percent
+    assert res[0] / res[1] <= bound
 
 
 def test_hbm_read_probe_reads_every_byte_once():

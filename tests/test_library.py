@@ -187,3 +187,26 @@ def test_fused_router_argument_checks():
     assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, None, None) == moe.ERR_NULL_ARG
     zero = moe.make_dims(0, 256, 16, 4, 64)
     assert lib.moe_route_fused(ctypes.byref(zero), fake, fake, None, None, fake, None) == moe.OK
+
+
+def test_audit_argument_checks():
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    d = moe.make_dims(64, 256, 16, 4, 64, 64)
+    assert lib.moe_audit_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.moe_audit_workspace_bytes(ctypes.byref(d), 5000) == 0
+    assert lib.moe_audit_workspace_bytes(ctypes.byref(d), 16) > 16 * 5 * (256 + 64) * 4
+    w = moe.moe_weights(fake, fake, fake, fake, None, None, None, fake, fake, fake)
+    n = lib.moe_audit_workspace_bytes(ctypes.byref(d), 4)
+    assert lib.moe_audit(ctypes.byref(d), ctypes.byref(w), None, fake, fake, fake, 4, None, fake, fake, n,
+                         None) == moe.ERR_NULL_ARG
+    assert lib.moe_audit(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake, 4, None, fake, fake, n - 1,
+                         None) == moe.ERR_WORKSPACE
+    assert lib.moe_audit(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake, 0, None, fake, fake, n,
+                         None) == moe.ERR_BAD_DIMS
+    wide = moe.make_dims(64, 32768, 16, 4, 64)
+    assert lib.moe_audit(ctypes.byref(wide), ctypes.byref(w), fake, fake, fake, fake, 4, None, fake, fake, 1 << 30,
+                         None) == moe.ERR_UNSUPPORTED
+    fp8 = moe.make_dims(64, 256, 16, 4, 64, w="e4m3")
+    assert lib.moe_audit(ctypes.byref(fp8), ctypes.byref(w), fake, fake, fake, fake, 4, None, fake, fake, 1 << 30,
+                         None) == moe.ERR_NULL_ARG                              # scales missing
