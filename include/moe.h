@@ -63,7 +63,8 @@ enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL_ARG = -1,    /* a required pointer is NULL */
   MOE_ERR_BAD_DIMS = -2,    /* T < 0, D/E/I/top_k < 1, top_k > E, expert slice outside [0, E) */
-  MOE_ERR_UNSUPPORTED = -3, /* dtype combination, D or I not a multiple of 64, E > 1024, top_k > 32 */
+  MOE_ERR_UNSUPPORTED = -3, /* dtype combination, D or I not a multiple of 64, E > 1024, top_k > 32,
+                               one expert's or the router's weight matrix of 2 GiB or more */
   MOE_ERR_WORKSPACE = -4,   /* ws_bytes smaller than moe_workspace_bytes(dims) */
   MOE_ERR_HIP = -5          /* a kernel launch failed (see moe_last_hip_error) */
 };

@@ -40,6 +40,13 @@ int check_dims(const moe_dims* d) {
   // every row index and byte offset below fits the kernels' integer types
   const int64_t tk = static_cast<int64_t>(d->T) * d->top_k;
   if (tk > (1ll << 30) || static_cast<int64_t>(d->T) * d->E > (1ll << 31) - 1) return MOE_ERR_UNSUPPORTED;
+  // one expert's (and the router's) weight matrix is addressed with 32-bit offsets
+  const int64_t wsz = d->w_dtype == MOE_F32 ? 4 : d->w_dtype == MOE_BF16 ? 2 : 1;
+  const int64_t lim = 1ll << 31;
+  if (static_cast<int64_t>(d->I) * d->D * wsz >= lim ||
+      static_cast<int64_t>(d->I_shared) * d->D * act_size(d->act_dtype) >= lim ||
+      static_cast<int64_t>(d->E) * d->D * act_size(d->act_dtype) >= lim)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

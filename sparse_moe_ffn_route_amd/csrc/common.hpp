@@ -47,6 +47,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) 
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, -1, 0x00020000);
 }
 
+// A resource with no records: every load through it is out of range, returns zeros and
+// touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_empty() {
+  return __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+}
+
 // NT: non-temporal hint (stream the lines through the caches without keeping them).
 template <bool NT = false>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -129,6 +135,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// Wave-uniform read of a value no thread writes during the kernel (e.g. a prefix
+// array written by an earlier launch), through the scalar data cache: it is counted
+// apart from the vector loads, so waiting for it never waits for a pending weight
+// stream.  Reads only.
+template <typename T>
+__device__ __forceinline__ T ld_scalar(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
 }
 
 // Map a linear block index onto a contiguous range of logical tiles per XCD.

@@ -17,15 +17,18 @@
 //     LDS.  Lane l of a wave reads 16 bytes of channel (l % 16) at K-byte offset
 //     (l / 16) * 16, so one wave step covers 16 rows x 64 contiguous bytes; K blocks
 //     of KSTEPS steps rotate through a ring of NBUF register buffers, so the loads of
-//     the next NBUF - 1 blocks are in flight while one block is multiplied;
+//     the next NBUF - 1 blocks are in flight while one block is multiplied.  They are
+//     buffer loads (a wave-uniform resource and offset plus one fixed offset per lane),
+//     so the loop computes no per-lane addresses and no load waits on a register that
+//     the compiler took from a pending load;
 //   * token rows are the MFMA "B" operand, shared by the 4 waves: staged per K block in
 //     LDS (double-buffered, one barrier per block), loaded before the weights of the
 //     same block so the LDS store never waits for the weight stream;
 //   * 16-row token fragments past the tile's last row are skipped (uniform branch), so
 //     a ragged group costs MFMA time in 16-row steps only.
-// Two shapes are instantiated: a streaming shape (MF = 1 or 2, two buffers, two
-// workgroups per CU; the down projection takes 4 fragments per wave to double the
-// channels each workgroup streams) for the few-rows-per-expert decode regime, where
+// Two shapes are instantiated: a streaming shape (MF = 1 or 2, a ring of two to four K
+// blocks; the down projection takes 4 fragments per wave to double the channels each
+// workgroup streams) for the few-rows-per-expert decode regime, where
 // each weight byte feeds one tile and the kernel is an HBM stream; and a tile shape
 // (MF = 16, 2-step blocks, three buffers, 2 fragments per matrix per wave, one
 // workgroup per CU so a wave may hold 512 registers) for the prefill regime: a 256-row
@@ -71,11 +74,20 @@ template <> struct OutStore<EL_BF16> {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-template <bool NT>
-__device__ __forceinline__ u32x4 load_weight(const uint8_t* p) {
-  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return *reinterpret_cast<const u32x4*>(p);
-}
+// One tile's coordinates and operand bases (wave-uniform).
+struct TileInfo {
+  bool sec;                  // a tile of the second problem
+  int g, row0;               // group, and its first row in the grouped order
+  int n_tile, ks;            // N-tile, K split
+  int rbeg, nrows;           // first row of the M-tile within the group, rows in use
+  int N, Kb_row, Kb, kofs;   // output width; bytes per weight row, per K range; K range offset
+  int nfull, tail_steps;     // full K blocks; 64-byte steps of a last partial block
+  const uint8_t* A;          // token rows (K range offset applied)
+  const int32_t* perm;
+  size_t lda_b;
+  const uint8_t* W0;
+  const uint8_t* W1;
+};
 
 template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED,
           int TDEPTH>
@@ -91,63 +103,71 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   constexpr int CPT = CHUNKS / 256;   // 16-byte token chunks per thread per K block
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LDS_ROW];
 
-  // ---- which tile ---------------------------------------------------------
+  // ---- tiles ----------------------------------------------------------------
   const int nt0 = (p0.N + BN - 1) / BN;
   const int nt1 = has_p1 ? (p1.N + BN - 1) / BN : 1;
-  const int tiles0 = (p0.offsets ? p0.tile_prefix[p0.n_groups] : (p0.rows + BM - 1) / BM * p0.k_splits) * nt0;
+  const int tiles0 = (p0.offsets ? ld_scalar(p0.tile_prefix + p0.n_groups) : (p0.rows + BM - 1) / BM * p0.k_splits) * nt0;
   const int tiles1 = has_p1 ? ((p1.rows + BM - 1) / BM) * p1.k_splits * nt1 : 0;
   const int total = tiles0 + tiles1;
-  if (static_cast<int>(blockIdx.x) >= total) return;
-  int L = xcd_remap(blockIdx.x, total);
-  const bool sec = L >= tiles0;
-  if (sec) L -= tiles0;
-#define SEL(f) (sec ? p1.f : p0.f)
-  const int n_tiles = sec ? nt1 : nt0;
-  const int32_t* offsets = SEL(offsets);
-  int g = 0, row0 = 0, count = SEL(rows), n_tile, m, ks = 0;
-  const int ksp = SEL(k_splits);
-  if (offsets) {
-    // group g owns tiles [pre[g] * n_tiles, pre[g + 1] * n_tiles), ordered (N-tile, M-tile)
-    const int32_t* pre = SEL(tile_prefix);
-    const int q = L / n_tiles;
-    int lo = 0, hi = SEL(n_groups) - 1;
-    while (lo < hi) {  // largest g with pre[g] <= q
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= q) lo = mid; else hi = mid - 1;
+#define SELT(s, f) ((s) ? p1.f : p0.f)
+  // Tile L of the launch order (ordered (group, N-tile, M-tile) within each problem).
+  auto locate = [&](int L) {
+    TileInfo t;
+    t.sec = L >= tiles0;
+    if (t.sec) L -= tiles0;
+    const int n_tiles = t.sec ? nt1 : nt0;
+    const int32_t* offsets = SELT(t.sec, offsets);
+    int g = 0, row0 = 0, count = SELT(t.sec, rows), n_tile, m, ks = 0;
+    const int ksp = SELT(t.sec, k_splits);
+    if (offsets) {
+      // group g owns tiles [pre[g] * n_tiles, pre[g + 1] * n_tiles), ordered (N-tile, M-tile)
+      const int32_t* pre = SELT(t.sec, tile_prefix);
+      const int q = L / n_tiles;
+      int lo = 0, hi = SELT(t.sec, n_groups) - 1;
+      while (lo < hi) {  // largest g with pre[g] <= q
+        const int mid = (lo + hi + 1) >> 1;
+        if (ld_scalar(pre + mid) <= q) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+      const int pg = ld_scalar(pre + g);
+      const int mt = ld_scalar(pre + g + 1) - pg;
+      const int local = L - pg * n_tiles;
+      n_tile = local / mt;
+      m = local % mt;
+      row0 = ld_scalar(offsets + g);
+      count = ld_scalar(offsets + g + 1) - row0;
+    } else {
+      const int mt = (count + BM - 1) / BM;
+      m = L % mt;
+      ks = (L / mt) % ksp;
+      n_tile = L / mt / ksp;
     }
-    g = lo;
-    const int mt = pre[g + 1] - pre[g];
-    const int local = L - pre[g] * n_tiles;
-    n_tile = local / mt;
-    m = local % mt;
-    row0 = offsets[g];
-    count = offsets[g + 1] - row0;
-  } else {
-    const int mt = (count + BM - 1) / BM;
-    m = L % mt;
-    ks = (L / mt) % ksp;
-    n_tile = L / mt / ksp;
-  }
-  // the tile coordinates are wave-uniform; say so, so that addresses built from them
-  // stay in scalar registers
-  g = __builtin_amdgcn_readfirstlane(g);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  count = __builtin_amdgcn_readfirstlane(count);
-  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
-  m = __builtin_amdgcn_readfirstlane(m);
-  ks = __builtin_amdgcn_readfirstlane(ks);
-  const int rbeg = m * BM;
-  const int nrows = min(BM, count - rbeg);
-  const int N = SEL(N);
-  const int Kb_row = SEL(K) * ES;  // bytes per row
-  const int Kb = Kb_row / ksp;     // bytes of this K range
-  const int kofs = ks * Kb;
-  const uint8_t* A = static_cast<const uint8_t*>(SEL(a)) + kofs;
-  const int32_t* perm = SEL(perm);
-  const size_t lda_b = static_cast<size_t>(SEL(lda)) * ES;
-  const size_t wgrp = static_cast<size_t>(g) * SEL(w_stride) * ES;
-  const uint8_t* W0 = static_cast<const uint8_t*>(SEL(w0)) + wgrp;
-  const uint8_t* W1 = SWIGLU ? static_cast<const uint8_t*>(SEL(w1)) + wgrp : nullptr;
+    // the tile coordinates are wave-uniform; say so, so that addresses built from them
+    // stay in scalar registers
+    t.g = __builtin_amdgcn_readfirstlane(g);
+    t.row0 = __builtin_amdgcn_readfirstlane(row0);
+    count = __builtin_amdgcn_readfirstlane(count);
+    t.n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+    m = __builtin_amdgcn_readfirstlane(m);
+    t.ks = __builtin_amdgcn_readfirstlane(ks);
+    t.rbeg = m * BM;
+    t.nrows = min(BM, count - t.rbeg);
+    t.N = SELT(t.sec, N);
+    t.Kb_row = SELT(t.sec, K) * ES;    // bytes per row
+    t.Kb = t.Kb_row / ksp;             // bytes of this K range
+    t.kofs = t.ks * t.Kb;
+    t.A = static_cast<const uint8_t*>(SELT(t.sec, a)) + t.kofs;
+    t.perm = SELT(t.sec, perm);
+    t.lda_b = static_cast<size_t>(SELT(t.sec, lda)) * ES;
+    const size_t wgrp = static_cast<size_t>(t.g) * SELT(t.sec, w_stride) * ES;
+    t.W0 = static_cast<const uint8_t*>(SELT(t.sec, w0)) + wgrp;
+    t.W1 = SWIGLU ? static_cast<const uint8_t*>(SELT(t.sec, w1)) + wgrp : nullptr;
+    // Full K blocks run a branch-free pipeline; a last partial block (K*ES not a
+    // multiple of KBLK) is handled after it with per-step guards.
+    t.nfull = t.Kb / KBLK;
+    t.tail_steps = (t.Kb - t.nfull * KBLK) / 64;
+    return t;
+  };
   // Weight addressing: row-major rows are Kb_row apart and a 64-byte step is 64 bytes on;
   // in the packed layout a 16-row fragment is one run of 1 KB per step.
   constexpr int SSTEP = PACKED ? 1024 : 64;     // bytes between consecutive 64-byte K steps
@@ -155,28 +175,24 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int ncol0 = n_tile * BN + wave * NF * 16;
-  const int mf_active = (nrows + 15) / 16;
-
-  // Full K blocks run a branch-free pipeline; a last partial block (K*ES not a
-  // multiple of KBLK) is handled after it with per-step guards.
-  const int nfull = Kb / KBLK;
-  const int tail_steps = (Kb - nfull * KBLK) / 64;
 
   // ---- epilogue: scales, SwiGLU, store --------------------------------------
-  auto epilogue = [&](const f32x4 (&acc)[NMAT][NF][MF]) {
-    void* out = static_cast<uint8_t*>(SEL(out)) + static_cast<size_t>(ks) * SEL(out_split_stride) * (OUT == EL_F32 ? 4 : 2);
-    const size_t ldo = SEL(ldo);
-    const float* a_scale = SEL(a_scale);
-    const float* s0 = SEL(s0);
-    const float* s1 = SEL(s1);
+  auto epilogue = [&](const TileInfo& t, const f32x4 (&acc)[NMAT][NF][MF]) {
+    void* out = static_cast<uint8_t*>(SELT(t.sec, out)) +
+                static_cast<size_t>(t.ks) * SELT(t.sec, out_split_stride) * (OUT == EL_F32 ? 4 : 2);
+    const size_t ldo = SELT(t.sec, ldo);
+    const float* a_scale = SELT(t.sec, a_scale);
+    const float* s0 = SELT(t.sec, s0);
+    const float* s1 = SELT(t.sec, s1);
+    const int N = t.N;
+    const int ncol0 = t.n_tile * BN + wave * NF * 16;
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
       const int r = mf * 16 + lrow;
-      if (r >= nrows) continue;
-      const int grow = row0 + rbeg + r;
+      if (r >= t.nrows) continue;
+      const int grow = t.row0 + t.rbeg + r;
       float as = 1.0f;
-      if (EL == EL_E4M3) as = a_scale[perm ? perm[grow] : grow];
+      if (EL == EL_E4M3) as = a_scale[t.perm ? t.perm[grow] : grow];
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
         const int n = ncol0 + nf * 16 + lgrp * 4;
@@ -186,10 +202,10 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x0 = acc[0][nf][mf][i];
-          if (EL == EL_E4M3) x0 *= as * s0[static_cast<size_t>(g) * N + min(n + i, N - 1)];
+          if (EL == EL_E4M3) x0 *= as * s0[static_cast<size_t>(t.g) * N + min(n + i, N - 1)];
           if (SWIGLU) {
             float x1 = acc[NMAT - 1][nf][mf][i];
-            if (EL == EL_E4M3) x1 *= as * s1[static_cast<size_t>(g) * N + min(n + i, N - 1)];
+            if (EL == EL_E4M3) x1 *= as * s1[static_cast<size_t>(t.g) * N + min(n + i, N - 1)];
             v[i] = silu(x0) * x1;
           } else {
             v[i] = x0;
@@ -202,6 +218,17 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 
   if constexpr (MF >= 8) {
     // ---- tile shape ---------------------------------------------------------
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    const TileInfo ti = locate(xcd_remap(blockIdx.x, total));
+    const int N = ti.N, Kb_row = ti.Kb_row, kofs = ti.kofs;
+    const int row0 = ti.row0, rbeg = ti.rbeg, nrows = ti.nrows, n_tile = ti.n_tile;
+    const int nfull = ti.nfull, tail_steps = ti.tail_steps;
+    const int32_t* perm = ti.perm;
+    const size_t lda_b = ti.lda_b;
+    const uint8_t* A = ti.A;
+    const uint8_t* W0 = ti.W0;
+    const uint8_t* W1 = ti.W1;
+    const int mf_active = (nrows + 15) / 16;
     // Weights and token rows are read through buffer resources: a wave-uniform base, a
     // fixed 32-bit offset per lane, and the K-block offset as the uniform part, so the
     // loop computes no per-lane addresses (the host keeps every offset below 2^31).
@@ -385,7 +412,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
         __syncthreads();
         mm(wr[0], buf, tail_steps);
       }
-      epilogue(acc);
+      epilogue(ti, acc);
     };
     static_assert(MF % kFragGroup == 0, "tile height must be whole fragment groups");
     switch ((mf_active + kFragGroup - 1) / kFragGroup) {
@@ -400,28 +427,41 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     }
   } else {
     // ---- streaming shapes -----------------------------------------------------
-    f32x4 acc[NMAT][NF][MF];
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    const TileInfo ti = locate(xcd_remap(blockIdx.x, total));
+    const int nfull = ti.nfull, tail_steps = ti.tail_steps;
+    const int mf_active = (ti.nrows + 15) / 16;
+    static_assert(NBUF >= 2 && NBUF <= 4, "streaming ring of 2 to 4 blocks");
+
+    // Weights as buffer loads: a resource per matrix at the group's weights, a fixed
+    // 32-bit offset per lane and fragment, and a wave-uniform offset per fragment to which
+    // the K-block offset is added.  The ring's loads then need no per-lane address
+    // arithmetic and no registers beyond their destinations, so the compiler never takes
+    // a pending load's registers for an address (which would wait for that load).
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    __amdgpu_buffer_rsrc_t wres[NMAT];
+    wres[0] = buffer_rsrc(ti.W0);
+    if (SWIGLU) wres[NMAT - 1] = buffer_rsrc(ti.W1);
+    uint32_t wvo[NF], wso[NF];
+    {
+      const int ncol0 = ti.n_tile * BN + wv * NF * 16;
 #pragma unroll
-    for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // ---- operand pointers ---------------------------------------------------
-    const uint8_t* wrow[NMAT][NF];
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf) {
-      size_t off;
-      if (PACKED) {
-        const int frag = min((ncol0 + nf * 16) / 16, N / 16 - 1);
-        off = (static_cast<size_t>(frag) * (Kb_row / 64) + kofs / 64) * 1024 + lane * 16;
-      } else {
-        const int n = min(ncol0 + nf * 16 + lrow, N - 1);
-        off = static_cast<size_t>(n) * Kb_row + kofs + lgrp * 16;
+      for (int nf = 0; nf < NF; ++nf) {
+        if (PACKED) {
+          const int frag = min((ncol0 + nf * 16) / 16, ti.N / 16 - 1);
+          wso[nf] = (static_cast<uint32_t>(frag) * (ti.Kb_row / 64) + ti.kofs / 64) * 1024;
+          wvo[nf] = lane * 16;
+        } else {
+          const int n = min(ncol0 + nf * 16 + lrow, ti.N - 1);
+          wso[nf] = ti.kofs;
+          wvo[nf] = static_cast<uint32_t>(n) * ti.Kb_row + lgrp * 16;
+        }
       }
-      wrow[0][nf] = W0 + off;
-      if (SWIGLU) wrow[NMAT - 1][nf] = W1 + off;
     }
+    // Token chunks: thread -> (row in the tile, byte column); rows past the tile's last
+    // row re-read that row (their output rows are never stored), so every token load is
+    // unconditional.  Token rows stay 64-bit addressed: this shape also serves inputs
+    // past 2 GiB.
     const uint8_t* arow[CPT];
     int acol[CPT], aoff[CPT];
 #pragma unroll
@@ -430,42 +470,41 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
       const int r = c / (KBLK / 16);
       acol[i] = (c % (KBLK / 16)) * 16;
       aoff[i] = r * LDS_ROW + acol[i];
-      arow[i] = nullptr;
-      if (r < nrows) {
-        const int grow = row0 + rbeg + r;
-        const int src = perm ? perm[grow] : grow;
-        arow[i] = A + static_cast<size_t>(src) * lda_b;
-      }
+      const int grow = ti.row0 + ti.rbeg + min(r, ti.nrows - 1);
+      const int src = ti.perm ? ti.perm[grow] : grow;
+      arow[i] = ti.A + static_cast<size_t>(src) * ti.lda_b;
     }
+    // Prefetches past the last block go through an empty resource: they return zeros
+    // without touching memory, so the ring's tail needs no branch.
+    const __amdgpu_buffer_rsrc_t none = buffer_rsrc_empty();
 
-
-    // Loads of K block kb; past the last block (kb >= nfull) every lane reads the same
-    // 64 bytes at the start of the first token row instead, which stay in L2, so the
-    // ring's tail prefetch costs no memory traffic and the loop needs no branch.
-    const uint8_t* dummy = A + (lane & 3) * 16;
     auto load_w = [&](u32x4 (&w)[NMAT][NF][KSTEPS], int kb) {
       const bool real = kb < nfull;
-      const size_t off = static_cast<size_t>(real ? kb : 0) * SBLK;
+      const uint32_t off = static_cast<uint32_t>(real ? kb : 0) * SBLK;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int a = 0; a < NMAT; ++a)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
-            w[a][nf][s] = load_weight<NTW>(real ? wrow[a][nf] + off + s * SSTEP : dummy);
+            w[a][nf][s] = buffer_load16<NTW>(real ? wres[a] : none, wvo[nf], wso[nf] + off + s * SSTEP);
     };
-    auto load_a = [&](u32x4 (&av)[CPT], int kb, int bytes) {
+    auto load_a = [&](u32x4 (&av)[CPT], int kb) {
       const int off = kb * KBLK;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        av[i] = u32x4{0u, 0u, 0u, 0u};
-        if (arow[i] && acol[i] < bytes) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + off + acol[i]);
-      }
+      for (int i = 0; i < CPT; ++i) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + off + acol[i]);
     };
     auto store_a = [&](const u32x4 (&av)[CPT], int buf) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&sA[buf][aoff[i]]) = av[i];
     };
+    f32x4 acc[NMAT][NF][MF];
+#pragma unroll
+    for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[a][nf][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto step = [&](const u32x4 (&w)[NMAT][NF][KSTEPS], int buf, int s) {
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
@@ -509,41 +548,63 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     };
 
     // Weight ring of NBUF K blocks: block b lives in buffer b % NBUF and is requested
-    // NBUF - 1 blocks before it is multiplied.  Prefetches past the last block read the
-    // L2-resident dummy instead of being guarded, so the loop body has no data-dependent
-    // branches.
+    // NBUF - 1 blocks before it is multiplied; token rows of block b + 1 are staged in LDS
+    // buffer (b + 1) & 1 while block b is multiplied.
     u32x4 wb[NBUF][NMAT][NF][KSTEPS];
     u32x4 av[CPT];
     if (nfull > 0) {
-      load_a(av, 0, KBLK);
+      load_a(av, 0);
 #pragma unroll
       for (int j = 0; j < NBUF - 1; ++j) load_w(wb[j], j);
       store_a(av, 0);
       __syncthreads();
-      for (int kb = 0; kb < nfull; kb += NBUF) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          if (j > 0 && kb + j >= nfull) break;
-          load_a(av, min(kb + j + 1, nfull - 1), KBLK);
-          load_w(wb[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
-          compute(wb[j], (kb + j) & 1);
-          store_a(av, (kb + j + 1) & 1);
-          __syncthreads();
-        }
+      // Whole ring turns, then a part turn of the blocks left over.  A whole turn has no
+      // exit inside, so at the top of the loop every load of the previous turn is known to
+      // have been consumed and nothing there waits for the loads still in flight.  The
+      // token loads of a block go out before its weight loads: the wait for them at the
+      // end of the block then leaves the block's weight loads in flight.
+      auto block = [&](auto jc, int kb) {
+        constexpr int j = decltype(jc)::value;
+        load_a(av, min(kb + j + 1, nfull - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wb[(j + NBUF - 1) % NBUF], kb + j + NBUF - 1);
+        compute(wb[j], (kb + j) & 1);
+        store_a(av, (kb + j + 1) & 1);
+        __syncthreads();
+      };
+      const int kb_full = nfull - nfull % NBUF;
+      int kb = 0;
+      for (; kb < kb_full; kb += NBUF) {
+        block(std::integral_constant<int, 0>{}, kb);
+        block(std::integral_constant<int, 1>{}, kb);
+        if constexpr (NBUF > 2) block(std::integral_constant<int, 2>{}, kb);
+        if constexpr (NBUF > 3) block(std::integral_constant<int, 3>{}, kb);
+      }
+      if (kb < nfull) {
+        block(std::integral_constant<int, 0>{}, kb);
+        if (kb + 1 < nfull) block(std::integral_constant<int, 1>{}, kb);
+        if constexpr (NBUF > 2) if (kb + 2 < nfull) block(std::integral_constant<int, 2>{}, kb);
+        if constexpr (NBUF > 3) if (kb + 3 < nfull) block(std::integral_constant<int, 3>{}, kb);
       }
     }
     if (tail_steps > 0) {
+      // a last partial K block: per-step guards
       const int buf = nfull & 1;
-      load_a(av, nfull, tail_steps * 64);
+      const int tb = tail_steps * 64;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        av[i] = u32x4{0u, 0u, 0u, 0u};
+        if (acol[i] < tb) av[i] = *reinterpret_cast<const u32x4*>(arow[i] + nfull * KBLK + acol[i]);
+      }
       store_a(av, buf);
-      const size_t off = static_cast<size_t>(nfull) * SBLK;
+      const uint32_t off = static_cast<uint32_t>(nfull) * SBLK;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int a = 0; a < NMAT; ++a)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
-            if (s < tail_steps) wb[0][a][nf][s] = load_weight<NTW>(wrow[a][nf] + off + s * SSTEP);
+            if (s < tail_steps) wb[0][a][nf][s] = buffer_load16<NTW>(wres[a], wvo[nf], wso[nf] + off + s * SSTEP);
       __syncthreads();
       if constexpr (kPairs) {
 #pragma unroll
@@ -555,9 +616,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
           if (s < tail_steps) step(wb[0], buf, s);
       }
     }
-    epilogue(acc);
+    epilogue(ti, acc);
   }
-#undef SEL
+#undef SELT
 }
 
 // Shape of a launch: tile height, K-block depth, weight ring depth, weight load kind,
