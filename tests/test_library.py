@@ -86,7 +86,9 @@ def test_hbm_read_probe_argument_checks():
 
 UNSUPPORTED = [dict(D=96), dict(I=100), dict(I_shared=32), dict(E=2048, top_k=2), dict(E=64, top_k=33),
                dict(act="f32", w="bf16"), dict(act="f32", w="f32", out="bf16"), dict(act="bf16", w="f32"),
-               dict(act="e4m3", w="e4m3")]
+               dict(act="e4m3", w="e4m3"),
+               # one expert's weight matrix (I x D) or the router's (E x D) of 2 GiB or more
+               dict(D=65536, I=16384, I_shared=0), dict(D=1 << 20, E=1024, I=64, I_shared=0)]
 
 
 @pytest.mark.parametrize("kw", BAD_DIMS)
