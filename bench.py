@@ -150,11 +150,14 @@ class Layer:
         layer_bytes = expert_w + shared_w + router_w + io
         layer_flop = (0 if wl.routing_given else 2 * wl.T * wl.D * wl.E) + n_a * 6 * wl.D * wl.I \
             + wl.T * 6 * wl.D * wl.I_shared
-        # gate/up kernel: gate+up weights of every active expert and of the shared expert,
-        # x read once, h written once
+        # routed gate/up kernel: gate+up weights (and fp8 scales) of every active expert,
+        # the gathered tokens' rows of x read once, h written once
+        x_rows = int((self.packed[:, 0, :].long() - wl.expert_begin).ge(0).logical_and(
+            (self.packed[:, 0, :].long() - wl.expert_begin).lt(wl.local)).any(dim=1).sum().item())
+        xb = 1 if wl.w == "e4m3" else ab  # fp8 experts read the e4m3 copy of x (and a scale per row)
         gu_bytes = active * (2 * wl.D * wl.I * wb + (2 * wl.I * 4 if wl.w == "e4m3" else 0)) \
-            + 2 * wl.D * wl.I_shared * ab + wl.T * wl.D * ab + n_a * wl.I * hb + wl.T * wl.I_shared * hb
-        gu_flop = n_a * 4 * wl.D * wl.I + wl.T * 4 * wl.D * wl.I_shared
+            + x_rows * (wl.D * xb + (4 if wl.w == "e4m3" else 0)) + n_a * wl.I * hb
+        gu_flop = n_a * 4 * wl.D * wl.I
         return dict(n_assign=n_a, active_experts=active, max_rows=int(counts.max().item()),
                     layer_bytes=layer_bytes, layer_flop=layer_flop, gate_up_bytes=gu_bytes, gate_up_flop=gu_flop)
 
@@ -178,10 +181,9 @@ def roofline_of(layer, stages):
     w = layer.work()
     t = stages["gate_up"] * 1e-3
     achieved = w["gate_up_bytes"] / t / 1e9
-    shared = " + shared expert" if layer.wl.I_shared else ""
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(layer.wl.name),
-            "kernel": f"gemm_kernel<{layer.wl.w},SwiGLU> (grouped gate/up{shared})",
+            "kernel": f"gemm_kernel<{layer.wl.w},SwiGLU> (routed grouped gate/up)",
             "bytes_per_launch": w["gate_up_bytes"], "avg_launch_ms": round(stages["gate_up"], 4),
             "mfma_TFLOPs": round(w["gate_up_flop"] / t / 1e12, 1)}
 

@@ -221,10 +221,11 @@ int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int3
  *   stage_events NULL, or MOE_STAGE_EVENTS caller-created hipEvent_t handles (as
  *              void*) that are recorded on `stream` at the stage boundaries: [0] before
  *              routing, [1] after routing, [2] after grouping (and the fp8 quantisation
- *              of x), [3] after the gate/up GEMM, [4] after the down GEMM, [5] after the
- *              combine.  Only for timing; the kernels are the same either way.
+ *              of x), [3] after the routed gate/up GEMM, [4] after the routed down GEMM
+ *              (and the fp8 quantisation of h), [5] after the shared expert's two GEMMs,
+ *              [6] after the combine.  Only for timing; the kernels are the same either way.
  */
-#define MOE_STAGE_EVENTS 6
+#define MOE_STAGE_EVENTS 7
 int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const void* x,
                       const int32_t* packed_in, const float* logit_bias, void* y, float* logits_out,
                       int32_t* packed_out, void* ws, size_t ws_bytes, void* const* stage_events,

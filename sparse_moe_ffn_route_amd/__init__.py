@@ -217,8 +217,8 @@ def make_weights(w_router=None, w_gate=None, w_up=None, w_down=None, s_gate=None
                                            sh_gate, sh_up, sh_down)])
 
 
-STAGE_EVENTS = 6   # MOE_STAGE_EVENTS
-STAGES = ("route", "permute", "gate_up", "down", "combine")
+STAGE_EVENTS = 7   # MOE_STAGE_EVENTS
+STAGES = ("route", "permute", "gate_up", "down", "shared", "combine")
 
 
 def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, logits_out=None, packed_out=None,

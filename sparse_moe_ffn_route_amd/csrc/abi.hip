@@ -192,7 +192,7 @@ int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* 
     const int shape = router_shape(d);
     const int bm = gemm_bm(shape), bn = gemm_bn(false, shape);
     const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn) * splits;
-    MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, false, p, nullptr, tiles, s));
+    MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, false, p, tiles, s));
     return hip_status(launch_route(parts, splits, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
   }
   return hip_status(launch_route(nullptr, 1, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
@@ -205,7 +205,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                     const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
                     void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
                     const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
-                    hipStream_t s) {
+                    hipEvent_t ev_down, hipStream_t s) {
   const int shape = expert_shape(d, perm != nullptr);
   const bool packed = d.weight_layout == MOE_LAYOUT_PACKED;
   const int bm = gemm_bm(shape);
@@ -226,19 +226,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   const GemmProblem g0 = problem(a_rows, perm, a_scale, d.D, offsets, tp_a, d.n_local, 0, w_gate, w_up, s_gate, s_up,
                                  static_cast<long long>(d.I) * d.D, h, d.I, d.I, d.D);
   const int tiles_gu = routed_tile_bound(tk, d.n_local, bm, d.I, bn_gu);
-  GemmProblem gs{};
-  if (shared)
-    gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr, nullptr, 0, h_sh,
-                 d.I_shared, d.I_shared, d.D);
-  if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, packed, g0, &gs, tiles_gu, s));
-  } else {
-    MOE_TRY(launch_gemm(w_el(d), hel, true, shape, packed, g0, nullptr, tiles_gu, s));
-    if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, hel, true, shape, packed, gs, nullptr,
-                          ((d.T + bm - 1) / bm) * ((d.I_shared + bn_gu - 1) / bn_gu), s));
-  }
-
+  MOE_TRY(launch_gemm(w_el(d), hel, true, shape, packed, g0, tiles_gu, s));
   if (ev_gate_up) MOE_TRY(hipEventRecord(ev_gate_up, s));
 
   // down projection of every grouped row
@@ -254,18 +242,26 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   const GemmProblem d0 = problem(h_in, nullptr, h_scale, d.I, offsets, tp_b, d.n_local, 0, w_down, nullptr, s_down,
                                  nullptr, static_cast<long long>(d.D) * d.I, out_rows, d.D, d.D, d.I);
   const int tiles_dn = routed_tile_bound(tk, d.n_local, bm, d.D, bn_dn);
-  GemmProblem ds{};
-  if (shared)
-    ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr, nullptr, nullptr, 0,
-                 sh_out, d.D, d.D, d.I_shared);
   const int oel = d.out_dtype;
-  if (shared && !fp8) {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, packed, d0, &ds, tiles_dn, s));
-  } else {
-    MOE_TRY(launch_gemm(w_el(d), oel, false, shape, packed, d0, nullptr, tiles_dn, s));
-    if (shared)
-      MOE_TRY(launch_gemm(d.act_dtype, oel, false, shape, packed, ds, nullptr,
-                          ((d.T + bm - 1) / bm) * ((d.D + bn_dn - 1) / bn_dn), s));
+  MOE_TRY(launch_gemm(w_el(d), oel, false, shape, packed, d0, tiles_dn, s));
+  if (ev_down) MOE_TRY(hipEventRecord(ev_down, s));
+
+  // The shared expert runs in launches of its own: as a second problem of the routed
+  // launches its tiles (all full, and last in the launch order) landed on one XCD.  Where
+  // the routed GEMMs stream 16-row tiles it takes 32-row ones: all T rows read the same
+  // weights, and taller tiles halve those re-reads.
+  if (shared) {
+    const int sh_shape = shape == kShapeStream16 ? kShapeStream32 : shape;
+    const int sh_bm = gemm_bm(sh_shape);
+    const int bn_g = gemm_bn(true, sh_shape), bn_d = gemm_bn(false, sh_shape);
+    const GemmProblem gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr,
+                                   nullptr, 0, h_sh, d.I_shared, d.I_shared, d.D);
+    MOE_TRY(launch_gemm(d.act_dtype, hel, true, sh_shape, packed, gs,
+                        ((d.T + sh_bm - 1) / sh_bm) * ((d.I_shared + bn_g - 1) / bn_g), s));
+    const GemmProblem ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr,
+                                   nullptr, nullptr, 0, sh_out, d.D, d.D, d.I_shared);
+    MOE_TRY(launch_gemm(d.act_dtype, oel, false, sh_shape, packed, ds,
+                        ((d.T + sh_bm - 1) / sh_bm) * ((d.D + bn_d - 1) / bn_d), s));
   }
   return MOE_OK;
 }
@@ -351,7 +347,7 @@ int moe_grouped_ffn(const moe_dims* dims, const void* a_rows, const float* a_sca
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
   return experts_forward(d, ws, L, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr,
+                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr, nullptr,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -426,13 +422,14 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   void* sh_out = d.I_shared ? at<void>(ws, L.sh_out) : nullptr;
   st = experts_forward(d, ws, L, a_rows, a_scale, perm, offsets, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up,
                        w->s_down, out_rows, x, d.I_shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, sh_out, true,
-                       stage_events ? static_cast<hipEvent_t>(stage_events[3]) : nullptr, s);
+                       stage_events ? static_cast<hipEvent_t>(stage_events[3]) : nullptr,
+                       stage_events ? static_cast<hipEvent_t>(stage_events[4]) : nullptr, s);
   if (st != MOE_OK) return st;
-  MOE_TRY(mark(4));
+  MOE_TRY(mark(5));
 
   // 4. unpermute + weighted combine (+ shared)
   MOE_TRY(launch_combine(d.out_dtype, out_rows, packed, inv, sh_out, d.T, d.D, d.top_k, y, s));
-  return hip_status(mark(5));
+  return hip_status(mark(6));
 }
 
 size_t moe_audit_workspace_bytes(const moe_dims* dims, int32_t n_sample) {

@@ -76,7 +76,6 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // One tile's coordinates and operand bases (wave-uniform).
 struct TileInfo {
-  bool sec;                  // a tile of the second problem
   int g, row0;               // group, and its first row in the grouped order
   int n_tile, ks;            // N-tile, K split
   int rbeg, nrows;           // first row of the M-tile within the group, rows in use
@@ -91,7 +90,7 @@ struct TileInfo {
 
 template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED,
           int TDEPTH>
-__global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmProblem p1, int has_p1) {
+__global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
   constexpr int NMAT = SWIGLU ? 2 : 1;
@@ -104,26 +103,19 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LDS_ROW];
 
   // ---- tiles ----------------------------------------------------------------
-  const int nt0 = (p0.N + BN - 1) / BN;
-  const int nt1 = has_p1 ? (p1.N + BN - 1) / BN : 1;
-  const int tiles0 = (p0.offsets ? ld_scalar(p0.tile_prefix + p0.n_groups) : (p0.rows + BM - 1) / BM * p0.k_splits) * nt0;
-  const int tiles1 = has_p1 ? ((p1.rows + BM - 1) / BM) * p1.k_splits * nt1 : 0;
-  const int total = tiles0 + tiles1;
-#define SELT(s, f) ((s) ? p1.f : p0.f)
+  const int n_tiles = (p.N + BN - 1) / BN;
+  const int total = (p.offsets ? ld_scalar(p.tile_prefix + p.n_groups) : (p.rows + BM - 1) / BM * p.k_splits) * n_tiles;
   // Tile L of the launch order (ordered (group, N-tile, M-tile) within each problem).
   auto locate = [&](int L) {
     TileInfo t;
-    t.sec = L >= tiles0;
-    if (t.sec) L -= tiles0;
-    const int n_tiles = t.sec ? nt1 : nt0;
-    const int32_t* offsets = SELT(t.sec, offsets);
-    int g = 0, row0 = 0, count = SELT(t.sec, rows), n_tile, m, ks = 0;
-    const int ksp = SELT(t.sec, k_splits);
+    const int32_t* offsets = p.offsets;
+    int g = 0, row0 = 0, count = p.rows, n_tile, m, ks = 0;
+    const int ksp = p.k_splits;
     if (offsets) {
       // group g owns tiles [pre[g] * n_tiles, pre[g + 1] * n_tiles), ordered (N-tile, M-tile)
-      const int32_t* pre = SELT(t.sec, tile_prefix);
+      const int32_t* pre = p.tile_prefix;
       const int q = L / n_tiles;
-      int lo = 0, hi = SELT(t.sec, n_groups) - 1;
+      int lo = 0, hi = p.n_groups - 1;
       while (lo < hi) {  // largest g with pre[g] <= q
         const int mid = (lo + hi + 1) >> 1;
         if (ld_scalar(pre + mid) <= q) lo = mid; else hi = mid - 1;
@@ -152,16 +144,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     t.ks = __builtin_amdgcn_readfirstlane(ks);
     t.rbeg = m * BM;
     t.nrows = min(BM, count - t.rbeg);
-    t.N = SELT(t.sec, N);
-    t.Kb_row = SELT(t.sec, K) * ES;    // bytes per row
+    t.N = p.N;
+    t.Kb_row = p.K * ES;               // bytes per row
     t.Kb = t.Kb_row / ksp;             // bytes of this K range
     t.kofs = t.ks * t.Kb;
-    t.A = static_cast<const uint8_t*>(SELT(t.sec, a)) + t.kofs;
-    t.perm = SELT(t.sec, perm);
-    t.lda_b = static_cast<size_t>(SELT(t.sec, lda)) * ES;
-    const size_t wgrp = static_cast<size_t>(t.g) * SELT(t.sec, w_stride) * ES;
-    t.W0 = static_cast<const uint8_t*>(SELT(t.sec, w0)) + wgrp;
-    t.W1 = SWIGLU ? static_cast<const uint8_t*>(SELT(t.sec, w1)) + wgrp : nullptr;
+    t.A = static_cast<const uint8_t*>(p.a) + t.kofs;
+    t.perm = p.perm;
+    t.lda_b = static_cast<size_t>(p.lda) * ES;
+    const size_t wgrp = static_cast<size_t>(t.g) * p.w_stride * ES;
+    t.W0 = static_cast<const uint8_t*>(p.w0) + wgrp;
+    t.W1 = SWIGLU ? static_cast<const uint8_t*>(p.w1) + wgrp : nullptr;
     // Full K blocks run a branch-free pipeline; a last partial block (K*ES not a
     // multiple of KBLK) is handled after it with per-step guards.
     t.nfull = t.Kb / KBLK;
@@ -178,12 +170,11 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
 
   // ---- epilogue: scales, SwiGLU, store --------------------------------------
   auto epilogue = [&](const TileInfo& t, const f32x4 (&acc)[NMAT][NF][MF]) {
-    void* out = static_cast<uint8_t*>(SELT(t.sec, out)) +
-                static_cast<size_t>(t.ks) * SELT(t.sec, out_split_stride) * (OUT == EL_F32 ? 4 : 2);
-    const size_t ldo = SELT(t.sec, ldo);
-    const float* a_scale = SELT(t.sec, a_scale);
-    const float* s0 = SELT(t.sec, s0);
-    const float* s1 = SELT(t.sec, s1);
+    void* out = static_cast<uint8_t*>(p.out) + static_cast<size_t>(t.ks) * p.out_split_stride * (OUT == EL_F32 ? 4 : 2);
+    const size_t ldo = p.ldo;
+    const float* a_scale = p.a_scale;
+    const float* s0 = p.s0;
+    const float* s1 = p.s1;
     const int N = t.N;
     const int ncol0 = t.n_tile * BN + wave * NF * 16;
 #pragma unroll
@@ -618,7 +609,6 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p0, GemmPro
     }
     epilogue(ti, acc);
   }
-#undef SELT
 }
 
 // Shape of a launch: tile height, K-block depth, weight ring depth, weight load kind,
@@ -645,46 +635,36 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIG
 };
 
 template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
-hipError_t launch_one(const GemmProblem& p0, const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
+hipError_t launch_one(const GemmProblem& p, int max_tiles, hipStream_t stream) {
   using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
   constexpr int NF = gemm_nf(SWIGLU, SHAPE);
-  constexpr int BM = 16 * S::MF, BN = 4 * NF * 16;
-  int tiles1 = 0;
-  GemmProblem q1 = p0;
-  if (p1) {
-    q1 = *p1;
-    tiles1 = ((p1->rows + BM - 1) / BM) * p1->k_splits * ((p1->N + BN - 1) / BN);
-  }
-  const int grid = max_tiles0 + tiles1;
-  if (grid == 0) return hipSuccess;
+  if (max_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH>),
-                     dim3(grid), dim3(256), 0, stream, p0, q1, p1 ? 1 : 0);
+                     dim3(max_tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int EL, int OUT, bool SWIGLU, bool PACKED>
-hipError_t launch_layout(int shape, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0,
-                         hipStream_t stream) {
+hipError_t launch_layout(int shape, const GemmProblem& p, int max_tiles, hipStream_t stream) {
   switch (shape) {
-    case kShapeStream16: return launch_one<EL, OUT, SWIGLU, kShapeStream16, PACKED>(p0, p1, max_tiles0, stream);
-    case kShapeStream32: return launch_one<EL, OUT, SWIGLU, kShapeStream32, PACKED>(p0, p1, max_tiles0, stream);
-    default: return launch_one<EL, OUT, SWIGLU, kShapeTile256, PACKED>(p0, p1, max_tiles0, stream);
+    case kShapeStream16: return launch_one<EL, OUT, SWIGLU, kShapeStream16, PACKED>(p, max_tiles, stream);
+    case kShapeStream32: return launch_one<EL, OUT, SWIGLU, kShapeStream32, PACKED>(p, max_tiles, stream);
+    default: return launch_one<EL, OUT, SWIGLU, kShapeTile256, PACKED>(p, max_tiles, stream);
   }
 }
 
 template <int EL, int OUT, bool SWIGLU>
-hipError_t launch_shape(int shape, bool packed, const GemmProblem& p0, const GemmProblem* p1, int max_tiles0,
-                        hipStream_t stream) {
-  return packed ? launch_layout<EL, OUT, SWIGLU, true>(shape, p0, p1, max_tiles0, stream)
-                : launch_layout<EL, OUT, SWIGLU, false>(shape, p0, p1, max_tiles0, stream);
+hipError_t launch_shape(int shape, bool packed, const GemmProblem& p, int max_tiles, hipStream_t stream) {
+  return packed ? launch_layout<EL, OUT, SWIGLU, true>(shape, p, max_tiles, stream)
+                : launch_layout<EL, OUT, SWIGLU, false>(shape, p, max_tiles, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p0,
-                       const GemmProblem* p1, int max_tiles0, hipStream_t stream) {
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p, int max_tiles,
+                       hipStream_t stream) {
 #define MOE_GEMM(E_, O_, S_) \
-  return launch_shape<E_, O_, S_>(shape, packed, p0, p1, max_tiles0, stream)
+  return launch_shape<E_, O_, S_>(shape, packed, p, max_tiles, stream)
   if (swiglu) {
     if (el == EL_F32 && out_el == EL_F32) MOE_GEMM(EL_F32, EL_F32, true);
     if (el == EL_BF16 && out_el == EL_BF16) MOE_GEMM(EL_BF16, EL_BF16, true);

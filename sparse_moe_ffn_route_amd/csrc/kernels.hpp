@@ -106,14 +106,14 @@ hipError_t launch_quant_rows(int in_el, const void* src, int rows, const int32_t
 hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int bm1, int32_t* prefix0,
                               int32_t* prefix1, hipStream_t stream);
 
-// Grouped GEMM over up to two problems in one launch (p1 may be NULL).
+// Grouped GEMM of one problem.
 //   swiglu: out = silu(A W0^T) * (A W1^T);  else out = A W0^T.
 //   el: operand type (EL_F32 / EL_BF16 / EL_E4M3); out_el: EL_F32 / EL_BF16.
 //   shape: kShapeStream16 / kShapeStream32 / kShapeTile256.
 //   packed: weights in the fragment-major layout of moe_pack_weights (else row-major).
-//   max_tiles0: host upper bound of p0's tiles (its grid share).
-hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p0,
-                       const GemmProblem* p1, int max_tiles0, hipStream_t stream);
+//   max_tiles: host upper bound of the problem's tiles (the grid; surplus workgroups exit).
+hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p, int max_tiles,
+                       hipStream_t stream);
 
 // Repack n_mats row-major [rows][row_bytes] matrices into the fragment-major layout.
 // Streaming read of bytes (multiple of 16) at src; sink receives one word per workgroup
