@@ -228,6 +228,9 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
     if stage_events is not None:
         if len(stage_events) != STAGE_EVENTS:
             raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
+        for e in stage_events:
+            if not e.cuda_event:
+                e.record()   # torch creates the underlying hipEvent on its first record
         ev = (ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
     _check_io(dims, x=x, logits=logits_out, packed=packed_in, bias=logit_bias, y=y)
     _need(packed_out, dims.T * 2 * dims.top_k * 4, "packed_out")

@@ -198,8 +198,8 @@ int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* 
   return hip_status(launch_route(nullptr, 1, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
 }
 
-// gate/up -> h (+ quantise) -> down for the routed groups, with an optional shared
-// expert evaluated as one more problem of the same launches.
+// gate/up -> h (+ quantise) -> down for the routed groups, then the optional shared
+// expert in launches of its own.
 int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_rows, const float* a_scale,
                     const int32_t* perm, const int32_t* offsets, const void* w_gate, const void* w_up,
                     const void* w_down, const float* s_gate, const float* s_up, const float* s_down,

@@ -179,6 +179,28 @@ def test_layer_forward_two_calls_reuse_workspace():
     np.testing.assert_array_equal(a["packed"], b["packed"])
 
 
+def test_stage_events_time_the_same_layer():
+    """Stage events only mark the stream: y is bit-identical, and the marks are in stage order."""
+    wl = MID["decode_like_bf16"]
+    dev = synth.make_inputs(wl, 3, "cpu").to("cuda")
+    d = dims_of(wl)
+    ws = moe.workspace(d)
+    w = moe.make_weights(dev.w_router, dev.w_gate, dev.w_up, dev.w_down, None, None, None,
+                         dev.ws_gate, dev.ws_up, dev.ws_down)
+    ys = []
+    for timed in (False, True):
+        y = torch.empty(wl.T, wl.D, dtype=torch.bfloat16, device="cuda")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_EVENTS)] if timed else None
+        moe.moe_layer_forward(d, w, dev.x, None, None, y, stage_events=evs, ws=ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu())
+    assert len(moe.STAGES) == moe.STAGE_EVENTS - 1
+    spans = [evs[i].elapsed_time(evs[i + 1]) for i in range(moe.STAGE_EVENTS - 1)]
+    assert all(t >= 0.0 for t in spans), spans
+    assert spans[moe.STAGES.index("shared")] > 0.0       # the shared expert has launches of its own
+    torch.testing.assert_close(ys[0], ys[1], rtol=0, atol=0)
+
+
 def test_expert_parallel_slices_sum_to_full_layer():
     """Eight slices run one after another sum to the full routed layer (what a reduce-scatter adds)."""
     full = W("ep_full", T=256, D=256, E=64, top_k=4, I=128, I_shared=0, act="bf16", w="bf16", out="f32",
