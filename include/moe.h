@@ -300,7 +300,8 @@ const char* moe_status_string(int status);
 /* hipError_t of the last failed launch on the calling host thread (0 if none). */
 int moe_last_hip_error(void);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3 (3: MOE_STAGE_EVENTS became 7, with a mark after the shared
+ * expert; moe_audit and moe_audit_workspace_bytes were added). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -59,6 +59,9 @@ class moe_weights(ctypes.Structure):
 _lib = None
 
 
+ABI_VERSION = 3   # moe_abi_version() of the library these signatures describe
+
+
 def library() -> ctypes.CDLL:
     """Load ``libmoe_hip.so`` (raises if it is missing)."""
     global _lib
@@ -97,6 +100,9 @@ def library() -> ctypes.CDLL:
     lib.moe_last_hip_error.restype = i32
     lib.moe_abi_version.argtypes = []
     lib.moe_abi_version.restype = i32
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, this binding expects {ABI_VERSION}: "
+                          "rebuild it with `python -m sparse_moe_ffn_route_amd.build`")
     _lib = lib
     return lib
 

@@ -498,6 +498,6 @@ const char* moe_status_string(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 }  // extern "C"
