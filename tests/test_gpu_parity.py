@@ -57,6 +57,11 @@ MID = {
     "k_eq_E": W("k_eq_E", T=33, D=128, E=8, top_k=8, I=64, I_shared=0, act="bf16", w="bf16", out="bf16"),
     # a single token
     "one_token": W("one_token", T=1, D=256, E=16, top_k=4, I=128, I_shared=64, act="bf16", w="bf16", out="bf16"),
+    # the largest supported k: the combine sums four full batches of 8 slots
+    "k_max": W("k_max", T=40, D=128, E=48, top_k=32, I=64, I_shared=64, act="bf16", w="bf16", out="bf16"),
+    # k = 12 over a quarter of the experts: a ragged second batch of slots, most slots non-local
+    "slice_k12_f32out": W("slice_k12_f32out", T=90, D=320, E=64, top_k=12, I=64, I_shared=0, act="bf16",
+                          w="bf16", out="f32", expert_begin=40, n_local=16),
 }
 
 
