@@ -630,14 +630,16 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream32, SWI
   static constexpr bool NT = PACKED;
 };
 template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIGLU, PACKED> {
-  static constexpr int MF = 16, KSTEPS = 2, NBUF = 3, MINB = 1, TDEPTH = 2;
+  static constexpr bool kTwoPerCu = EL == EL_E4M3 && !SWIGLU;
+  static constexpr int MF = 16, KSTEPS = 2, NBUF = kTwoPerCu ? 2 : 3, MINB = kTwoPerCu ? 2 : 1;
+  static constexpr int TDEPTH = kTwoPerCu ? 1 : 2;
   static constexpr bool NT = PACKED;
 };
 
 template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
 hipError_t launch_one(const GemmProblem& p, int max_tiles, hipStream_t stream) {
   using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
-  constexpr int NF = gemm_nf(SWIGLU, SHAPE);
+  constexpr int NF = gemm_nf(SWIGLU, SHAPE, EL);
   if (max_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH>),
                      dim3(max_tiles), dim3(256), 0, stream, p);
