@@ -69,7 +69,7 @@ int router_splits(const moe_dims& d) {
   const int kblk = shape == kShapeTile256 ? 128 : 512;  // bytes per K block of the shape
   if (row_bytes % kblk) return 1;
   const int blocks = row_bytes / kblk;
-  const int bm = gemm_bm(shape), bn = gemm_bn(false, shape, d.act_dtype);
+  const int bm = gemm_bm(shape), bn = gemm_bn(false, shape, d.act_dtype, false);
   const int64_t tiles = static_cast<int64_t>((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn);
   int s = 1;
   if (shape == kShapeTile256) {
@@ -190,7 +190,7 @@ int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* 
     p.k_splits = splits;
     p.out_split_stride = static_cast<long long>(d.T) * d.E;
     const int shape = router_shape(d);
-    const int bm = gemm_bm(shape), bn = gemm_bn(false, shape, d.act_dtype);
+    const int bm = gemm_bm(shape), bn = gemm_bn(false, shape, d.act_dtype, false);
     const int tiles = ((d.T + bm - 1) / bm) * ((d.E + bn - 1) / bn) * splits;
     MOE_TRY(launch_gemm(d.act_dtype, EL_F32, false, shape, false, p, tiles, s));
     return hip_status(launch_route(parts, splits, logits, bias, d.T, d.E, d.top_k, d.renormalize, packed, s));
@@ -209,7 +209,7 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   const int shape = expert_shape(d, perm != nullptr);
   const bool packed = d.weight_layout == MOE_LAYOUT_PACKED;
   const int bm = gemm_bm(shape);
-  const int bn_gu = gemm_bn(true, shape, w_el(d)), bn_dn = gemm_bn(false, shape, w_el(d));
+  const int bn_gu = gemm_bn(true, shape, w_el(d), packed), bn_dn = gemm_bn(false, shape, w_el(d), packed);
   const int tk = d.T * d.top_k;
   const bool fp8 = d.w_dtype == MOE_E4M3;
   int32_t* tp_a = at<int32_t>(ws, L.tp_a);
@@ -253,7 +253,8 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   if (shared) {
     const int sh_shape = shape == kShapeStream16 ? kShapeStream32 : shape;
     const int sh_bm = gemm_bm(sh_shape);
-    const int bn_g = gemm_bn(true, sh_shape, d.act_dtype), bn_d = gemm_bn(false, sh_shape, d.act_dtype);
+    const int bn_g = gemm_bn(true, sh_shape, d.act_dtype, packed);
+    const int bn_d = gemm_bn(false, sh_shape, d.act_dtype, packed);
     const GemmProblem gs = problem(x_shared, nullptr, nullptr, d.D, nullptr, nullptr, 1, d.T, sh_gate, sh_up, nullptr,
                                    nullptr, 0, h_sh, d.I_shared, d.I_shared, d.D);
     MOE_TRY(launch_gemm(d.act_dtype, hel, true, sh_shape, packed, gs,

@@ -31,7 +31,8 @@
 // workgroup streams) for the few-rows-per-expert decode regime, where
 // each weight byte feeds one tile and the kernel is an HBM stream; and a tile shape
 // (MF = 16, 2-step blocks, three buffers, 2 fragments per matrix per wave, one
-// workgroup per CU so a wave may hold 512 registers) for the prefill regime: a 256-row
+// workgroup per CU so a wave may hold 512 registers; the expert down projections take
+// two workgroups per CU with a two-block ring) for the prefill regime: a 256-row
 // M-tile covers every row of a typical expert (~160 at 8K tokens), so each weight byte
 // is streamed from HBM once and feeds all of the expert's rows, and 32 channels per
 // matrix per wave halve the token bytes staged per MFMA; only experts with more rows
@@ -629,8 +630,13 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream32, SWI
   static constexpr int MF = 2, KSTEPS = 8, NBUF = 2, MINB = 2, TDEPTH = 1;
   static constexpr bool NT = PACKED;
 };
+// tile256 down projections of the experts (E4M3, or packed 16-bit weights; the router
+// projection keeps its row-major shape): K is short (I = 1024), so a tile runs few K
+// blocks and its prologue and epilogue weigh; 2 fragments per wave, a two-block ring
+// and one block of token lookahead fit two workgroups per CU, which overlap one
+// another's ends (the compiler spills ~32 VGPRs there; measured faster nonetheless).
 template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIGLU, PACKED> {
-  static constexpr bool kTwoPerCu = EL == EL_E4M3 && !SWIGLU;
+  static constexpr bool kTwoPerCu = !SWIGLU && (EL == EL_E4M3 || PACKED);
   static constexpr int MF = 16, KSTEPS = 2, NBUF = kTwoPerCu ? 2 : 3, MINB = kTwoPerCu ? 2 : 1;
   static constexpr int TDEPTH = kTwoPerCu ? 1 : 2;
   static constexpr bool NT = PACKED;
@@ -639,7 +645,7 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIG
 template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
 hipError_t launch_one(const GemmProblem& p, int max_tiles, hipStream_t stream) {
   using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
-  constexpr int NF = gemm_nf(SWIGLU, SHAPE, EL);
+  constexpr int NF = gemm_nf(SWIGLU, SHAPE, EL, PACKED);
   if (max_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH>),
                      dim3(max_tiles), dim3(256), 0, stream, p);

@@ -44,13 +44,16 @@ struct GemmProblem {
 enum : int { kShapeStream16 = 0, kShapeStream32 = 1, kShapeTile256 = 2 };
 
 constexpr int gemm_bm(int shape) { return shape == kShapeStream16 ? 16 : shape == kShapeStream32 ? 32 : 256; }
-// 16-column output fragments per wave (per matrix for SwiGLU).
-constexpr int gemm_nf(bool swiglu, int shape, int el) {
-  return shape == kShapeTile256 ? (swiglu || el == EL_E4M3 ? 2 : 4)
+// 16-column output fragments per wave (per matrix for SwiGLU).  el: weight element type;
+// packed: fragment-major weights.  Host tile counts and kernels both take it from here.
+constexpr int gemm_nf(bool swiglu, int shape, int el, bool packed) {
+  return shape == kShapeTile256 ? (swiglu || el == EL_E4M3 || packed ? 2 : 4)
                                 : shape == kShapeStream16 ? (swiglu ? 1 : 4) : (swiglu ? 1 : 2);
 }
 // Output channels per workgroup (4 waves).
-constexpr int gemm_bn(bool swiglu, int shape, int el) { return 4 * gemm_nf(swiglu, shape, el) * 16; }
+constexpr int gemm_bn(bool swiglu, int shape, int el, bool packed) {
+  return 4 * gemm_nf(swiglu, shape, el, packed) * 16;
+}
 
 // fp32 shadow of the layer on sampled tokens (numerical audit); element types are EL_*.
 struct AuditLaunch {
