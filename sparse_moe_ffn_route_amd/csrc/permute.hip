@@ -285,8 +285,62 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 // Per-row E4M3 quantisation: s = amax / 448 (1 for an all-zero row), q = E4M3(v / s).
 // One wave per row; rows counted by *n_rows_dev when given (device-side row count).
 // Rows of at most 4096 columns are read once: each lane issues the loads of all its
-// 8-column pieces together and keeps them in registers for both the amax and the
-// quantisation pass; wider rows are read twice.
+// 8-column pieces together (2, 4 or 8 of them, by row width) and keeps them in
+// registers for both the amax and the quantisation pass; wider rows are read twice.
+// One row held in registers: P 8-column pieces per lane (cols <= 512 * P).
+template <int IN, int P>
+__device__ __forceinline__ void quant_row_in_regs(const void* __restrict__ src, int r, int cols, int lane,
+                                                  uint8_t* __restrict__ dst, float* __restrict__ scale) {
+  // Branch-free loads: a piece past the row end re-reads the row's last piece and
+  // is masked out of the amax and not stored.
+  float v[P][8];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int c = min((i * kWave + lane) * 8, cols - 8);
+    if (IN == EL_BF16) {
+      const uint4 p =
+          *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + static_cast<size_t>(r) * cols + c);
+      const uint32_t wds[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[i][2 * q] = bf16_bits_to_f32(wds[q] & 0xFFFFu);
+        v[i][2 * q + 1] = bf16_bits_to_f32(wds[q] >> 16);
+      }
+    } else {
+      const float4* p =
+          reinterpret_cast<const float4*>(static_cast<const float*>(src) + static_cast<size_t>(r) * cols + c);
+      const float4 a = p[0], b = p[1];
+      v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+      v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const bool in_row = (i * kWave + lane) * 8 < cols;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, in_row ? fabsf(v[i][q]) : 0.0f);
+  }
+  amax = wave_max(amax);
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int c = (i * kWave + lane) * 8;
+    if (c >= cols) continue;
+    uint32_t packed4[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float a0 = fminf(fmaxf(v[i][4 * q + 0] / s, -448.0f), 448.0f);
+      const float a1 = fminf(fmaxf(v[i][4 * q + 1] / s, -448.0f), 448.0f);
+      const float a2 = fminf(fmaxf(v[i][4 * q + 2] / s, -448.0f), 448.0f);
+      const float a3 = fminf(fmaxf(v[i][4 * q + 3] / s, -448.0f), 448.0f);
+      packed4[q] = f32x2_to_e4m3x2(a0, a1) | (f32x2_to_e4m3x2(a2, a3) << 16);
+    }
+    *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * cols + c) = make_uint2(packed4[0], packed4[1]);
+  }
+  if (lane == 0) scale[r] = s;
+}
+
 template <int IN>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int rows,
                                                          const int32_t* __restrict__ n_rows_dev, int cols,
@@ -295,58 +349,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   const int lane = lane_id();
   const int n = n_rows_dev ? *n_rows_dev : rows;
   if (r >= n) return;
-  constexpr int kMaxPieces = 8;
-  if (cols <= kWave * 8 * kMaxPieces) {
-    // Branch-free loads: a piece past the row end re-reads the row's last piece and
-    // is masked out of the amax and not stored.
-    float v[kMaxPieces][8];
-#pragma unroll
-    for (int i = 0; i < kMaxPieces; ++i) {
-      const int c = min((i * kWave + lane) * 8, cols - 8);
-      if (IN == EL_BF16) {
-        const uint4 p =
-            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + static_cast<size_t>(r) * cols + c);
-        const uint32_t wds[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[i][2 * q] = bf16_bits_to_f32(wds[q] & 0xFFFFu);
-          v[i][2 * q + 1] = bf16_bits_to_f32(wds[q] >> 16);
-        }
-      } else {
-        const float4* p =
-            reinterpret_cast<const float4*>(static_cast<const float*>(src) + static_cast<size_t>(r) * cols + c);
-        const float4 a = p[0], b = p[1];
-        v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
-        v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
-      }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPieces; ++i) {
-      const bool in_row = (i * kWave + lane) * 8 < cols;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, in_row ? fabsf(v[i][q]) : 0.0f);
-    }
-    amax = wave_max(amax);
-    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPieces; ++i) {
-      const int c = (i * kWave + lane) * 8;
-      if (c >= cols) continue;
-      uint32_t packed4[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float a0 = fminf(fmaxf(v[i][4 * q + 0] / s, -448.0f), 448.0f);
-        const float a1 = fminf(fmaxf(v[i][4 * q + 1] / s, -448.0f), 448.0f);
-        const float a2 = fminf(fmaxf(v[i][4 * q + 2] / s, -448.0f), 448.0f);
-        const float a3 = fminf(fmaxf(v[i][4 * q + 3] / s, -448.0f), 448.0f);
-        packed4[q] = f32x2_to_e4m3x2(a0, a1) | (f32x2_to_e4m3x2(a2, a3) << 16);
-      }
-      *reinterpret_cast<uint2*>(dst + static_cast<size_t>(r) * cols + c) = make_uint2(packed4[0], packed4[1]);
-    }
-    if (lane == 0) scale[r] = s;
-    return;
-  }
+  if (cols <= kWave * 8 * 2) return quant_row_in_regs<IN, 2>(src, r, cols, lane, dst, scale);
+  if (cols <= kWave * 8 * 4) return quant_row_in_regs<IN, 4>(src, r, cols, lane, dst, scale);
+  if (cols <= kWave * 8 * 8) return quant_row_in_regs<IN, 8>(src, r, cols, lane, dst, scale);
   // each lane handles 8 consecutive values per step
   float amax = 0.0f;
   for (int c = lane * 8; c < cols; c += kWave * 8) {
