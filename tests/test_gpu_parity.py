@@ -62,6 +62,9 @@ MID = {
     # k = 12 over a quarter of the experts: a ragged second batch of slots, most slots non-local
     "slice_k12_f32out": W("slice_k12_f32out", T=90, D=320, E=64, top_k=12, I=64, I_shared=0, act="bf16",
                           w="bf16", out="f32", expert_begin=40, n_local=16),
+    # ~150 rows per expert (256-row tiles, one ragged M-tile each) with fp32 output from bf16 operands
+    "tile_bf16_f32out": W("tile_bf16_f32out", T=600, D=256, E=16, top_k=4, I=128, I_shared=64, act="bf16",
+                          w="bf16", out="f32"),
 }
 
 
@@ -90,7 +93,7 @@ def test_layer_forward_parity(name):
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "mid_fp32", "decode_like_bf16", "mid_bf16", "mid_bf16_f32out",
                                   "skew_bf16", "slice_fp8", "slice_fp8_f32out", "fp8_shared", "fp8_shared_tile",
-                                  "one_token"])
+                                  "one_token", "tile_bf16_f32out"])
 def test_layer_forward_parity_packed_weights(name):
     """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
     _check_layer(MID[name], seed=2, packed=True)
