@@ -69,6 +69,18 @@ enum moe_status {
   MOE_ERR_HIP = -5          /* a kernel launch failed (see moe_last_hip_error) */
 };
 
+/*
+ * Error word of a workspace: the int32 at byte offset MOE_WS_ERROR_OFFSET of `ws` holds,
+ * after a moe_permute or moe_layer_forward call on that workspace has run, the number of
+ * (token, slot) pairs of the routing blob whose expert id lies outside [0, E).  Such a
+ * pair is skipped like a pair of another device's expert; a non-zero count means the
+ * blob was corrupt (the blob may arrive from another device: Playbook, section "Fusing
+ * Three Collectives Into Two").  The word is rewritten by every such call (never
+ * accumulated), so it needs no clearing; read it after the call has completed on its
+ * stream.
+ */
+#define MOE_WS_ERROR_OFFSET 0
+
 /* Problem shape. */
 typedef struct moe_dims {
   int32_t T;            /* tokens (rows of x) */
@@ -154,8 +166,13 @@ int moe_route_fused(const moe_dims* dims, const void* x, const void* w_router, f
 
 /*
  * Permutation: group the (token, slot) pairs whose expert is local by expert
- * (experts ascending, (t, j) ascending inside an expert).  Ids outside the local
- * slice (other devices' experts, or any value outside [0, E)) are skipped.
+ * (experts ascending, (t, j) ascending inside an expert), the grouping that the
+ * grouped GEMMs and the later "unpermutation + local reduction" need (Playbook,
+ * introduction and table "Three High-Leverage Optimizations"); under expert
+ * parallelism only the device's own slice of experts is grouped (Playbook, section
+ * "Fusing Three Collectives Into Two").  Ids outside the local slice (other devices'
+ * experts) are skipped; ids outside [0, E) are skipped too and counted in the error
+ * word at ws + MOE_WS_ERROR_OFFSET.
  *
  *   packed     [T][2][top_k] int32 input
  *   counts     [n_local] int32 out: rows of each local expert
@@ -209,6 +226,14 @@ int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int3
 
 /*
  * The whole layer: route -> permute -> grouped experts (+ shared expert) -> combine.
+ * The layer of "3. Sparse Mixture-of-Experts (MoE)" (Tối ưu hóa ... TPU Ironwood):
+ * top-k routed experts plus the always-on shared expert; its dataflow of grouped GEMMs
+ * followed by unpermutation with a local reduction is the Playbook's (introduction and
+ * table "Three High-Leverage Optimizations"); with a local slice and given routing it is
+ * one device's expert-parallel share between the all-gather and the reduce-scatter
+ * (Playbook, "Fusing Three Collectives Into Two"; "Como o Google otimizou ...",
+ * section "O problema do sharding e a solução").  A given blob's ids outside [0, E)
+ * are counted in the error word at ws + MOE_WS_ERROR_OFFSET.
  *
  *   x          [T][D] act_dtype
  *   packed_in  [T][2][top_k] int32 or NULL.  Non-NULL: the routing is given (one
@@ -300,8 +325,8 @@ const char* moe_status_string(int status);
 /* hipError_t of the last failed launch on the calling host thread (0 if none). */
 int moe_last_hip_error(void);
 
-/* ABI version of this header: 3 (3: MOE_STAGE_EVENTS became 7, with a mark after the shared
- * expert; moe_audit and moe_audit_workspace_bytes were added). */
+/* ABI version of this header: 4 (3: MOE_STAGE_EVENTS became 7, with a mark after the shared
+ * expert; moe_audit and moe_audit_workspace_bytes were added; 4: the workspace error word). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

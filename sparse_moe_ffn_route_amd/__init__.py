@@ -31,6 +31,8 @@ _LAYOUT_CODE = {"rows": LAYOUT_ROWS, "packed": LAYOUT_PACKED}
 # enum moe_status
 OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 
+WS_ERROR_OFFSET = 0                     # MOE_WS_ERROR_OFFSET: byte offset of the workspace error word
+
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_route_fused", "moe_permute", "moe_grouped_ffn",
@@ -59,7 +61,7 @@ class moe_weights(ctypes.Structure):
 _lib = None
 
 
-ABI_VERSION = 3   # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 4   # moe_abi_version() of the library these signatures describe
 
 
 def library() -> ctypes.CDLL:
@@ -244,6 +246,11 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, ev, _stream(stream)),
            "moe_layer_forward")
+
+
+def workspace_error_count(ws: torch.Tensor) -> torch.Tensor:
+    """View of the workspace error word (ids outside [0, E) seen by the last grouping on ws), as int32 [1]."""
+    return ws[WS_ERROR_OFFSET:WS_ERROR_OFFSET + 4].view(torch.int32)
 
 
 def moe_audit(dims, weights: moe_weights, x, packed, y, sample, ref_out=None, stream=None):

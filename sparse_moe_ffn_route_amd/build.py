@@ -56,15 +56,29 @@ def _compile(hipcc, src, obj, extra):
     return "\n".join(noise)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source for gfx950 and link ``libmoe_hip.so``; returns its path."""
+def _stale(src, obj):
+    """True when obj is missing or older than src or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, extra_flags=(), incremental: bool = False) -> str:
+    """Compile every source for gfx950 and link ``libmoe_hip.so``; returns its path.
+
+    incremental: recompile only sources whose object is older than the source or a header.
+    """
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    todo = [(s, o) for s, o in zip(srcs, objs) if not incremental or _stale(s, o)]
     workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        futs = [ex.submit(_compile, hipcc, s, o, list(extra_flags)) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_compile, hipcc, s, o, list(extra_flags)) for s, o in todo]
         for f in futs:
             msg = f.result()
             if msg and verbose:
@@ -79,4 +93,4 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -81,7 +81,7 @@ int router_splits(const moe_dims& d) {
 }
 
 struct Layout {
-  size_t logits, logits_part, packed, hist, base, rank, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
+  size_t err, logits, logits_part, packed, hist, base, rank, bad, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
   size_t xq, sx, h, h_sh, hq, sh, out_rows, sh_out, total;
 };
 
@@ -97,6 +97,7 @@ Layout layout(const moe_dims& d) {
   const size_t U = perm_units(d.T, d.top_k);
   const bool fp8 = d.w_dtype == MOE_E4M3;
   const size_t hs = act_size(d.act_dtype), os = out_size(d.out_dtype);
+  L.err = take(4);  // MOE_WS_ERROR_OFFSET: first word of the workspace
   L.logits = take(T * d.E * 4);
   const int rs = router_splits(d);
   L.logits_part = take(rs > 1 ? static_cast<size_t>(rs) * T * d.E * 4 : 0);
@@ -104,6 +105,7 @@ Layout layout(const moe_dims& d) {
   L.hist = take(nl * U * 4);
   L.base = take(nl * U * 4);
   L.rank = take(tk * 4);
+  L.bad = take(U * 4);
   L.counts = take(nl * 4);
   L.offsets = take((nl + 1) * 4);
   L.tp_a = take((nl + 1) * 4);
@@ -317,9 +319,10 @@ int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.T == 0) return MOE_OK;
   const int bm = gemm_bm(expert_shape(d, true));
-  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm_token, inv_pos, bm, bm,
-                         at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), s));
+  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.E, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
+                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), at<int32_t>(ws, L.bad), counts, offsets,
+                         perm_token, inv_pos, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b),
+                         at<int32_t>(ws, L.err), s));
   if (x) {
     const int tk = d.T * d.top_k;
     if (fp8) {
@@ -405,10 +408,10 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   int32_t* perm = at<int32_t>(ws, L.perm_token);
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
   const int bm = gemm_bm(expert_shape(d, true));
-  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
-                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets, perm, inv, bm, bm,
-                         at<int32_t>(ws, L.tp_a),
-                         at<int32_t>(ws, L.tp_b), s));
+  MOE_TRY(launch_permute(packed, d.T, d.top_k, d.E, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
+                         at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), at<int32_t>(ws, L.bad), counts, offsets,
+                         perm, inv, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), at<int32_t>(ws, L.err),
+                         s));
   const void* a_rows = x;
   const float* a_scale = nullptr;
   if (fp8) {
@@ -499,6 +502,6 @@ const char* moe_status_string(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 }  // extern "C"

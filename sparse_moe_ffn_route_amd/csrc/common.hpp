@@ -137,6 +137,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 // Wave-uniform read of a value no thread writes during the kernel (e.g. a prefix
 // array written by an earlier launch), through the scalar data cache: it is counted
 // apart from the vector loads, so waiting for it never waits for a pending weight

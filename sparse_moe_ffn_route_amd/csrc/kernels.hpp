@@ -93,12 +93,14 @@ hipError_t launch_route(const float* parts, int n_parts, float* logits, const fl
                         int renormalize, int32_t* packed, hipStream_t stream);
 
 // Grouping by expert.  Also writes the M-tile prefixes of both grouped GEMMs (tile heights
-// bm0, bm1) into prefix0 / prefix1 ([n_local + 1]).
-//   hist, base: [perm_units(T, k)][n_local] scratch; rank: [T * k] scratch.
-hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
-                          int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                          int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0, int32_t* prefix1,
-                          hipStream_t stream);
+// bm0, bm1) into prefix0 / prefix1 ([n_local + 1]), and into *err_word the number of
+// pairs whose id lies outside [0, E) (skipped like any non-local pair).
+//   hist, base: [perm_units(T, k)][n_local] scratch; rank: [T * k] scratch;
+//   bad: [perm_units(T, k)] scratch.
+hipError_t launch_permute(const int32_t* packed, int T, int k, int E, int e_begin, int n_local, int32_t* hist,
+                          int32_t* base, int32_t* rank, int32_t* bad, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0,
+                          int32_t* prefix1, int32_t* err_word, hipStream_t stream);
 
 hipError_t launch_gather_rows(const void* src, const float* src_scale, const int32_t* perm_token,
                               const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,

@@ -33,25 +33,42 @@ __device__ __forceinline__ int local_expert(const int32_t* packed, int i, int k,
   return (e >= 0 && e < n_local) ? e : -1;
 }
 
+// Local expert of pair i as local_expert(), and whether its id lies outside [0, E) (a
+// corrupt or foreign blob: such a pair is skipped and counted).
+__device__ __forceinline__ int local_expert_checked(const int32_t* packed, int i, int k, int e_begin, int n_local,
+                                                    int E, bool& bad) {
+  const int t = i / k;
+  const int id = packed[static_cast<size_t>(t) * 2 * k + (i - t * k)];
+  bad = id < 0 || id >= E;
+  const int e = id - e_begin;
+  return (e >= 0 && e < n_local) ? e : -1;
+}
+
 // Stage 1 of the multi-workgroup grouping: one wave per unit of kPermUnit consecutive
 // pairs.  The wave loads all its pairs first (one memory latency), then walks them 64
 // at a time: lanes holding the same expert find each other with one ballot per id bit,
 // rank themselves by lane order, and the lowest lane advances that expert's running
-// count in LDS.  Output: each local pair's rank inside its unit, and hist[unit][e].
+// count in LDS.  Output: each local pair's rank inside its unit, hist[unit][e], and
+// bad[unit], the unit's pairs whose id lies outside [0, E).
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
-                                                        int e_begin, int n_local, int n_bits, int n_units,
-                                                        int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+                                                        int e_begin, int n_local, int E, int n_bits, int n_units,
+                                                        int32_t* __restrict__ rank, int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ bad) {
   __shared__ int32_t run[kWavesPerBlock][kMaxLocalExperts];
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int u = blockIdx.x * kWavesPerBlock + w;
   if (u >= n_units) return;  // whole wave leaves together; waves use disjoint LDS rows
   const int base_i = u * kPermUnit;
   int pe[kUnitSteps];
+  int n_bad = 0;  // wave-uniform
 #pragma unroll
   for (int s = 0; s < kUnitSteps; ++s) {
     const int i = base_i + s * kWave + lane;
-    pe[s] = i < n_pairs ? local_expert(packed, i, k, e_begin, n_local) : -1;
+    bool b = false;
+    pe[s] = i < n_pairs ? local_expert_checked(packed, i, k, e_begin, n_local, E, b) : -1;
+    n_bad += __popcll(__ballot(b));
   }
+  if (lane == 0) bad[u] = n_bad;
   for (int e = lane; e < n_local; e += kWave) run[w][e] = 0;
   __builtin_amdgcn_wave_barrier();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -78,13 +95,23 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
 // M-tile counts are scanned over experts; hist[unit][e] becomes base[unit][e], the first
 // grouped row of expert e coming from that unit.  Each pass over units reads one
 // contiguous row of n_local counts across the workgroup.
+// It also adds the units' counts of out-of-range ids into *err_word.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int n_local,
                                                          int n_units, int bm0, int bm1, int32_t* __restrict__ base,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ prefix0,
-                                                         int32_t* __restrict__ prefix1) {
+                                                         int32_t* __restrict__ prefix1,
+                                                         const int32_t* __restrict__ bad,
+                                                         int32_t* __restrict__ err_word) {
   __shared__ int32_t sc[3][1024];
+  __shared__ int32_t sbad[1024 / kWave];
   const int e = threadIdx.x;
+  {
+    int nb = 0;
+    for (int u = e; u < n_units; u += 1024) nb += bad[u];
+    nb = wave_sum_int(nb);
+    if (lane_id() == 0) sbad[e / kWave] = nb;
+  }
   int tot = 0;
   if (e < n_local) {
 #pragma unroll 8
@@ -125,6 +152,9 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     offsets[n_local] = sc[0][1023];
     prefix0[0] = 0;
     prefix1[0] = 0;
+    int nb = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) nb += sbad[w];  // sbad is complete: barriers above
+    *err_word = nb;
   }
 }
 
@@ -163,27 +193,35 @@ __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ perm_token,
                                                           int32_t* __restrict__ inv_pos, int32_t* __restrict__ prefix0,
-                                                          int32_t* __restrict__ prefix1) {
+                                                          int32_t* __restrict__ prefix1, int E,
+                                                          int32_t* __restrict__ err_word) {
   __shared__ int32_t hist[kFusedWaves][kMaxLocalExperts];
   __shared__ int32_t sc[3][1024];
+  __shared__ int32_t sbad[kFusedWaves];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const int per_wave = ((n_pairs + kFusedWaves * kWave - 1) / (kFusedWaves * kWave)) * kWave;
   const int lo = min(n_pairs, w * per_wave), hi = min(n_pairs, lo + per_wave);
   const int nsteps = (hi - lo + kWave - 1) / kWave;
 
   int pv[MAXSTEPS];  // -1: past the end; else (t << 11) | (local expert + 1 or 0)
+  int n_bad = 0;     // pairs of this wave whose id lies outside [0, E) (wave-uniform)
 #pragma unroll
   for (int s = 0; s < MAXSTEPS; ++s) {
     pv[s] = -1;
     if (s < nsteps) {
       const int i = lo + s * kWave + lane;
+      bool b = false;
       if (i < hi) {
         const int t = i / k;
-        const int e = packed[static_cast<size_t>(t) * 2 * k + (i - t * k)] - e_begin;
+        const int id = packed[static_cast<size_t>(t) * 2 * k + (i - t * k)];
+        b = id < 0 || id >= E;
+        const int e = id - e_begin;
         pv[s] = (t << 11) | ((e >= 0 && e < n_local) ? e + 1 : 0);
       }
+      n_bad += __popcll(__ballot(b));
     }
   }
+  if (lane == 0) sbad[w] = n_bad;
 
   for (int e = lane; e < n_local; e += kWave) hist[w][e] = 0;
   __builtin_amdgcn_wave_barrier();
@@ -235,6 +273,9 @@ __global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restr
     offsets[n_local] = sc[0][1023];
     prefix0[0] = 0;
     prefix1[0] = 0;
+    int nb = 0;
+    for (int v = 0; v < kFusedWaves; ++v) nb += sbad[v];  // written before the first barrier
+    *err_word = nb;
   }
   __syncthreads();
 
@@ -439,24 +480,24 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 
 }  // namespace
 
-hipError_t launch_permute(const int32_t* packed, int T, int k, int e_begin, int n_local, int32_t* hist,
-                          int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                          int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0, int32_t* prefix1,
-                          hipStream_t stream) {
+hipError_t launch_permute(const int32_t* packed, int T, int k, int E, int e_begin, int n_local, int32_t* hist,
+                          int32_t* base, int32_t* rank, int32_t* bad, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0,
+                          int32_t* prefix1, int32_t* err_word, hipStream_t stream) {
   const int n_pairs = T * k;
   int n_bits = 1;
   while ((1 << n_bits) < n_local) ++n_bits;
   if (n_pairs <= kFusedWaves * kWave * 8) {
     hipLaunchKernelGGL(perm_fused_kernel<8>, dim3(1), dim3(1024), 0, stream, packed, n_pairs, k, e_begin, n_local,
-                       n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1);
+                       n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1, E, err_word);
     return hipGetLastError();
   }
   const int n_units = perm_units(T, k);
   const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL(perm_rank_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
-                     n_bits, n_units, rank, hist);
+                     E, n_bits, n_units, rank, hist, bad);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, bm0, bm1, base,
-                     counts, offsets, prefix0, prefix1);
+                     counts, offsets, prefix0, prefix1, bad, err_word);
   hipLaunchKernelGGL(perm_place_kernel, dim3((n_pairs + 255) / 256), dim3(256), 0, stream, packed, n_pairs, k,
                      e_begin, n_local, n_units, base, rank, perm_token, inv_pos);
   return hipGetLastError();

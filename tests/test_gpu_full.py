@@ -2,9 +2,14 @@
 
 Every token's routing is checked bit-exactly (ids) against the oracle fed the
 GPU's fp32 logits, the grouping of all T*k pairs bit-exactly, the router logits
-on sampled tokens against the fp32 accumulation bound, and y on sampled tokens
-(the oracle evaluates only those tokens' experts; every row of the layer is
-independent, so this is exactly the oracle's value for those tokens).
+on sampled tokens against the fp32 accumulation bound, and y on EVERY token of
+the 512-token decode batches, the 8192-token prefill chunks and the fp8
+expert-parallel share, with and without the shared expert (the shared expert
+dominates y, so a routed-path error could hide under the tolerance with it on).
+The 32K-token probe checks y on tokens chosen to reach the grouped GEMMs' corner
+cases (the ragged last M-tile of the largest experts, rows 192-255 of 256-row
+tiles) plus random ones; every row of the layer is independent, so the oracle's
+value for those tokens is exact without evaluating the others.
 """
 
 import numpy as np
@@ -16,9 +21,9 @@ import sparse_moe_ffn_route_amd as moe
 import synth
 from harness import dims_of, gpu_layer, logit_bound, rel_err, tolerance
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-SAMPLE = 12
+SAMPLE_LOGITS = 32
 
 
 @pytest.fixture(scope="module")
@@ -40,11 +45,6 @@ def _variant(big, name):
                              big.ws_gate, big.ws_up, big.ws_down, bias, None)
 
 
-def _sample_tokens(T, seed):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(T, size=min(SAMPLE, T), replace=False))
-
-
 def _check_grouping(inp, packed_np):
     wl = inp.wl
     d = dims_of(wl)
@@ -53,50 +53,116 @@ def _check_grouping(inp, packed_np):
     offsets = torch.empty(wl.local + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     inv = torch.empty(T, k, dtype=torch.int32, device="cuda")
-    moe.moe_permute(d, torch.from_numpy(packed_np).cuda(), counts, offsets, perm, inv, ws=moe.workspace(d))
+    ws = moe.workspace(d)
+    moe.moe_permute(d, torch.from_numpy(packed_np).cuda(), counts, offsets, perm, inv, ws=ws)
     ids, _ = oracle.unpack_routing(packed_np)
     c, o, p, iv = oracle.permute(ids, wl.expert_begin, wl.local)
     np.testing.assert_array_equal(counts.cpu().numpy(), c)
     np.testing.assert_array_equal(offsets.cpu().numpy(), o)
     np.testing.assert_array_equal(perm.cpu().numpy()[: int(o[-1])], p)
     np.testing.assert_array_equal(inv.cpu().numpy(), iv)
-    return c
+    assert int(moe.workspace_error_count(ws).cpu()[0]) == 0
+    return c, o, p
 
 
-def _check_routed_layer(inp, seed, packed=True):
+def _routing(inp, g):
+    """Oracle routing of every token from the GPU's fp32 logits (or the given blob), checked against the GPU's."""
     wl = inp.wl
-    g = gpu_layer(inp, packed=packed)
-    # routing of every token, from the GPU's fp32 logits
+    if wl.routing_given:
+        np.testing.assert_array_equal(g["packed"], inp.packed.cpu().numpy())   # the given blob passes through
+        ids, w32 = oracle.unpack_routing(g["packed"])
+        return ids, w32.astype(np.float64)
     bias = None if inp.bias is None else inp.bias.cpu().numpy()
     ids, w = oracle.route(g["logits"], wl.top_k, bias=bias, renormalize=wl.renormalize)
     ids_gpu, w_gpu = oracle.unpack_routing(g["packed"])
     np.testing.assert_array_equal(ids_gpu, ids)
     np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
-    counts = _check_grouping(inp, g["packed"])
-    s = _sample_tokens(wl.T, seed)
+    # router logits on sampled tokens against the fp32 accumulation bound
+    s = np.sort(np.random.default_rng(wl.T).choice(wl.T, size=min(SAMPLE_LOGITS, wl.T), replace=False))
     x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
     wr = synth.f64(inp.w_router)
     l_ref = oracle.router_logits(x_s, wr).astype(np.float64)
     assert np.all(np.abs(g["logits"][s] - l_ref) <= logit_bound(x_s, wr, l_ref))
-    ref = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp), shared=synth.shared_f64(inp))
-    err = rel_err(g["y"][s], ref["y"])
-    assert err <= tolerance(wl), f"{wl.name}: sampled rel err {err:.3e}"
-    # the routed part alone (shared expert off) on the same tokens, row-major weights
+    return ids, w
+
+
+def _oracle(inp, ids, w, tokens=None):
+    """Oracle y with and without the shared expert on `tokens` (None: all), from one evaluation of the experts."""
+    wl = inp.wl
+    if tokens is None:
+        x = synth.f64(inp.x)
+    else:
+        x = synth.f64(inp.x[torch.from_numpy(tokens).cuda()])
+        ids, w = ids[tokens], w[tokens]
+    if wl.w == "e4m3":
+        res = oracle.layer_from_routing_fp8(x, ids, w, synth.ExpertViewFP8(inp), shared=synth.shared_f64(inp),
+                                            expert_begin=wl.expert_begin, n_local=wl.local)
+    else:
+        res = oracle.layer_from_routing(x, ids, w, synth.ExpertView(inp), shared=synth.shared_f64(inp),
+                                        expert_begin=wl.expert_begin, n_local=wl.local)
+    routed = oracle.combine(res["out_rows"], w, res["inv_pos"])
+    return res["y"], routed
+
+
+def _check_layer_full(inp, tokens=None):
+    """Packed weights with the shared expert (the bench's launch configuration), then row-major weights without it;
+    y compared on every token (or on `tokens`)."""
+    wl = inp.wl
+    print(f"[full] {wl.name}: layer on the GPU", flush=True)
+    g = gpu_layer(inp, packed=True)
+    ids, w = _routing(inp, g)
+    counts, offsets, perm = _check_grouping(inp, g["packed"])
+    if callable(tokens):
+        tokens = tokens(counts, offsets, perm)
     g2 = gpu_layer(inp, shared=False, packed=False)
-    ref2 = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp), shared=None)
-    err2 = rel_err(g2["y"][s], ref2["y"])
-    assert err2 <= tolerance(wl), f"{wl.name} (no shared): sampled rel err {err2:.3e}"
+    np.testing.assert_array_equal(g2["packed"], g["packed"])
+    print(f"[full] {wl.name}: oracle on {wl.T if tokens is None else len(tokens)} tokens", flush=True)
+    y_ref, routed_ref = _oracle(inp, ids, w, tokens)
+    sel = slice(None) if tokens is None else tokens
+    tol = tolerance(wl)
+    err = rel_err(g["y"][sel], y_ref)
+    assert err <= tol, f"{wl.name}: rel err {err:.3e}"
+    err2 = rel_err(g2["y"][sel], routed_ref)
+    assert err2 <= tol, f"{wl.name} (no shared expert): rel err {err2:.3e}"
+    if wl.expert_begin != 0 or wl.local != wl.E:
+        # tokens with no local expert get an all-zero partial sum
+        local = ((ids >= wl.expert_begin) & (ids < wl.expert_begin + wl.local)).any(axis=1)
+        none_local = np.nonzero(~local)[0]
+        assert none_local.size > 0 and np.all(g["y"][none_local] == 0)
+    print(f"[full] {wl.name}: rel err {err:.2e} (shared on), {err2:.2e} (routed only)", flush=True)
     return counts
 
 
 def test_decode_full_size(big_layer):
-    counts = _check_routed_layer(_variant(big_layer, "decode_bf16"), 10)
+    counts = _check_layer_full(_variant(big_layer, "decode_bf16"))
     assert counts.sum() == 512 * 10
 
 
 def test_prefill_full_size(big_layer):
-    counts = _check_routed_layer(_variant(big_layer, "prefill_bf16"), 11)
+    counts = _check_layer_full(_variant(big_layer, "prefill_bf16"))
     assert counts.sum() == 8192 * 10
+    assert counts.max() > 192                               # some experts fill rows 192-255 of their tile
+
+
+def test_skewed_prefill_full_size(big_layer):
+    counts = _check_layer_full(_variant(big_layer, "skew_prefill_bf16"))
+    assert (counts == 0).sum() == 32                      # the never-chosen experts stay empty
+    assert counts.max() / counts.mean() > 15              # a straggler expert many times the mean load
+
+
+def _corner_tokens(counts, offsets, perm, T, n_random=24, seed=15):
+    """Tokens whose grouped rows sit in the grouped GEMMs' corners: the ragged last 256-row M-tile of the three
+    largest experts, rows 192-255 of every M-tile of the largest experts, and random tokens."""
+    rows = []
+    for e in np.argsort(-counts, kind="stable")[:3]:
+        n = int(counts[e])
+        last = (n - 1) // 256 * 256
+        rows += list(range(offsets[e] + last, offsets[e] + n))[-8:]          # the ragged last tile's rows
+        for m0 in range(0, n, 256):
+            rows += [offsets[e] + r for r in range(m0 + 192, min(m0 + 256, n), 9)]
+    rng = np.random.default_rng(seed)
+    tok = set(perm[np.asarray(rows, dtype=np.int64)].tolist()) | set(rng.choice(T, n_random).tolist())
+    return np.array(sorted(tok), dtype=np.int64)
 
 
 def test_prefill32k_full_size(big_layer):
@@ -108,55 +174,25 @@ def test_prefill32k_full_size(big_layer):
     b = big_layer
     inp = synth.LayerInputs(wl, x, b.w_router, b.w_gate, b.w_up, b.w_down, None, None, None, b.ws_gate, b.ws_up,
                             b.ws_down, None, None)
-    counts = _check_routed_layer(inp, 15)
+    counts = _check_layer_full(inp, tokens=lambda c, o, p: _corner_tokens(c, o, p, wl.T))
     assert counts.sum() == 32768 * 10 and counts.min() > 256
-
-
-def test_skewed_prefill_full_size(big_layer):
-    counts = _check_routed_layer(_variant(big_layer, "skew_prefill_bf16"), 12)
-    assert (counts == 0).sum() == 32                      # the never-chosen experts stay empty
-    assert counts.max() / counts.mean() > 15              # a straggler expert many times the mean load
 
 
 def test_ep_share_fp8_full_size():
     wl = synth.WORKLOADS["ep_share_fp8"]
     inp = synth.make_inputs(wl, 0, "cuda")
-    g = gpu_layer(inp, packed=True)
-    np.testing.assert_array_equal(g["packed"], inp.packed.cpu().numpy())   # the given blob passes through
-    counts = _check_grouping(inp, g["packed"])
+    counts = _check_layer_full(inp)
     assert 9000 < counts.sum() < 11500                    # ~T*k*64/512 pairs are local
-    ids, w32 = oracle.unpack_routing(inp.packed.cpu().numpy())
-    local_tok = np.nonzero(((ids >= 0) & (ids < 64)).any(axis=1))[0]
-    s = np.sort(np.random.default_rng(13).choice(local_tok, size=SAMPLE, replace=False))
-    x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
-    ref = oracle.layer_from_routing_fp8(x_s, ids[s], w32[s].astype(np.float64), synth.ExpertViewFP8(inp),
-                                        expert_begin=0, n_local=64)
-    err = rel_err(g["y"][s], ref["y"])
-    assert err <= tolerance(wl), f"fp8 share: sampled rel err {err:.3e}"
-    # tokens with no local expert get an all-zero partial sum
-    none_local = np.nonzero(~((ids >= 0) & (ids < 64)).any(axis=1))[0]
-    assert none_local.size > 0 and np.all(g["y"][none_local] == 0)
+    del inp
+    torch.cuda.empty_cache()
 
 
 def test_decode_fp8_full_size():
     """The decode batch with e4m3 routed experts (router and shared expert bf16)."""
     wl = synth.WORKLOADS["decode_fp8"]
     inp = synth.make_inputs(wl, 0, "cuda")
-    g = gpu_layer(inp, packed=True)
-    ids, w = oracle.route(g["logits"], wl.top_k, renormalize=wl.renormalize)
-    ids_gpu, w_gpu = oracle.unpack_routing(g["packed"])
-    np.testing.assert_array_equal(ids_gpu, ids)
-    np.testing.assert_allclose(w_gpu, w, rtol=0, atol=1e-6)
-    counts = _check_grouping(inp, g["packed"])
+    counts = _check_layer_full(inp)
     assert counts.sum() == 512 * 10
-    s = _sample_tokens(wl.T, 14)
-    x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
-    wr = synth.f64(inp.w_router)
-    l_ref = oracle.router_logits(x_s, wr).astype(np.float64)
-    assert np.all(np.abs(g["logits"][s] - l_ref) <= logit_bound(x_s, wr, l_ref))
-    ref = oracle.layer_from_routing_fp8(x_s, ids[s], w[s], synth.ExpertViewFP8(inp), shared=synth.shared_f64(inp))
-    err = rel_err(g["y"][s], ref["y"])
-    assert err <= tolerance(wl), f"decode fp8: sampled rel err {err:.3e}"
     del inp
     torch.cuda.empty_cache()
 
@@ -170,7 +206,7 @@ def test_operands_past_2gib_take_the_streaming_shape():
     g = gpu_layer(inp, packed=True)
     ids, w = oracle.route(g["logits"], wl.top_k)
     np.testing.assert_array_equal(oracle.unpack_routing(g["packed"])[0], ids)
-    s = _sample_tokens(wl.T, 16)
+    s = np.sort(np.random.default_rng(16).choice(wl.T, size=64, replace=False))
     x_s = synth.f64(inp.x[torch.from_numpy(s).cuda()])
     ref = oracle.layer_from_routing(x_s, ids[s], w[s], synth.ExpertView(inp))
     err = rel_err(g["y"][s], ref["y"])

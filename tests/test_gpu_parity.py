@@ -65,6 +65,20 @@ MID = {
     # ~150 rows per expert (256-row tiles, one ragged M-tile each) with fp32 output from bf16 operands
     "tile_bf16_f32out": W("tile_bf16_f32out", T=600, D=256, E=16, top_k=4, I=128, I_shared=64, act="bf16",
                           w="bf16", out="f32"),
+    # ~256 rows per expert at D = 1024, I = 512: the 256-row tile kernels' K loops run 16 (gate/up) and 8
+    # (down) blocks, so their weight rings turn several times with a remainder; experts of 193-256 rows
+    # take the 14- and 16-fragment loops, experts past 256 rows a ragged second M-tile; the 2048-token
+    # router projection takes the 256-row tile shape with K splits
+    "tile_wide_bf16": W("tile_wide_bf16", T=2048, D=1024, E=32, top_k=4, I=512, I_shared=256, act="bf16",
+                        w="bf16", out="bf16"),
+    "tile_wide_fp8": W("tile_wide_fp8", T=2048, D=1024, E=32, top_k=4, I=512, I_shared=256, act="bf16",
+                       w="e4m3", out="bf16"),
+    # the same width with skewed popularity: a hot expert over several M-tiles, empty experts
+    "tile_wide_skew_bf16": W("tile_wide_skew_bf16", T=1536, D=1024, E=24, top_k=3, I=512, I_shared=0,
+                             act="bf16", w="bf16", out="bf16", skew_alpha=0.8, skew_s=1.1, skew_empty=3),
+    # fp8 expert-parallel slice at the same width with given routing (64-expert-share analogue)
+    "tile_wide_fp8_slice": W("tile_wide_fp8_slice", T=4096, D=1024, E=64, top_k=8, I=512, I_shared=0,
+                             act="bf16", w="e4m3", out="bf16", expert_begin=16, n_local=16, routing_given=True),
 }
 
 
@@ -93,7 +107,8 @@ def test_layer_forward_parity(name):
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "mid_fp32", "decode_like_bf16", "mid_bf16", "mid_bf16_f32out",
                                   "skew_bf16", "slice_fp8", "slice_fp8_f32out", "fp8_shared", "fp8_shared_tile",
-                                  "one_token", "tile_bf16_f32out"])
+                                  "one_token", "tile_bf16_f32out", "tile_wide_bf16", "tile_wide_fp8",
+                                  "tile_wide_skew_bf16", "tile_wide_fp8_slice"])
 def test_layer_forward_parity_packed_weights(name):
     """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
     _check_layer(MID[name], seed=2, packed=True)
@@ -171,7 +186,8 @@ def test_pack_weights_layout():
     np.testing.assert_array_equal(dst.reshape(-1), expect)
 
 
-@pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "tiny_fp32", "skew_bf16"])
+@pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "tiny_fp32", "skew_bf16", "tile_wide_bf16",
+                                  "tile_wide_fp8", "fp8_shared_tile"])
 def test_layer_forward_parity_without_shared_expert(name):
     """The shared expert dominates y; without it a routed-path error cannot hide under the tolerance."""
     _check_layer(MID[name], seed=1, shared=False)
@@ -358,6 +374,33 @@ def test_permute_bit_exact(T, k, E, begin, n_local, junk):
     n_a = int(o[-1])
     np.testing.assert_array_equal(perm.cpu().numpy()[:n_a], p)
     np.testing.assert_array_equal(inv.cpu().numpy(), iv)
+    # the workspace error word counts the ids outside [0, E), and is rewritten by the next call
+    n_bad = int(((ids < 0) | (ids >= E)).sum())
+    assert (n_bad > 0) == junk
+    assert int(moe.workspace_error_count(ws).cpu()[0]) == n_bad
+    clean = np.where((ids < 0) | (ids >= E), 0, ids).astype(np.int32)
+    moe.moe_permute(d, torch.from_numpy(oracle.pack_routing(clean, np.ones(ids.shape, np.float32))).cuda(), counts,
+                    offsets, perm, inv, ws=ws)
+    assert int(moe.workspace_error_count(ws).cpu()[0]) == 0
+
+
+def test_layer_with_corrupt_given_blob_skips_and_counts_bad_ids():
+    """A given blob with ids outside [0, E): those pairs contribute nothing and are counted."""
+    wl = MID["slice_fp8"]
+    inp = synth.make_inputs(wl, 7, "cpu")
+    ids, w32 = oracle.unpack_routing(inp.packed.numpy())
+    rng = np.random.default_rng(8)
+    m = rng.random(ids.shape) < 0.15
+    ids = ids.copy()
+    ids[m] = np.where(rng.random(int(m.sum())) < 0.5, -1 - rng.integers(0, 5, int(m.sum())),
+                      wl.E + rng.integers(0, 5, int(m.sum())))
+    inp.packed = torch.from_numpy(oracle.pack_routing(ids, w32))
+    d = dims_of(wl)
+    ws = moe.workspace(d)
+    g = gpu_layer(inp, ws=ws)
+    assert int(moe.workspace_error_count(ws).cpu()[0]) == int(m.sum())
+    ref = oracle_layer(inp)
+    assert rel_err(g["y"], ref["y"]) <= tolerance(wl)
 
 
 def test_permute_gathers_rows_and_quantises_fp8():

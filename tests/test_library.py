@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(moe.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_library_targets_gfx950_only():

@@ -180,6 +180,22 @@ def test_route_bias_shifts_and_excludes():
     assert (w[:, 0] > 1 - 1e-12).all()
 
 
+def test_pack_routing_plane_order_against_a_hand_written_blob():
+    """Plane 0 holds the ids, plane 1 the IEEE binary32 bit patterns of the weights, token-major
+    ([T][2][k]); the words below are written out by hand (0.75 = 0x3F400000, 0.25 = 0x3E800000,
+    0.5 = 0x3F000000, 1.0 = 0x3F800000, -0.0 = 0x80000000)."""
+    ids = np.array([[3, 1], [0, 7]], dtype=np.int32)
+    w = np.array([[0.75, 0.25], [1.0, -0.0]], dtype=np.float32)
+    blob = oracle.pack_routing(ids, w)
+    expect = np.array([[[3, 1], [0x3F400000, 0x3E800000]],
+                       [[0, 7], [0x3F800000, -0x80000000]]], dtype=np.int64).astype(np.int32)
+    assert blob.dtype == np.int32 and blob.shape == (2, 2, 2)
+    np.testing.assert_array_equal(blob, expect)
+    i2, w2 = oracle.unpack_routing(np.array([[[5, 6], [0x3F000000, 0x3F800000]]], dtype=np.int32))
+    np.testing.assert_array_equal(i2, [[5, 6]])
+    np.testing.assert_array_equal(w2, np.array([[0.5, 1.0]], dtype=np.float32))
+
+
 def test_pack_unpack_round_trip_bits():
     rng = np.random.default_rng(8)
     ids = rng.integers(0, 512, (33, 10)).astype(np.int32)
