@@ -32,10 +32,11 @@
  *     plane 1 the IEEE binary32 bits of the matching weights (token-major, so the
  *     blobs of several devices concatenate along tokens).
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL
- *     is the default stream).  The library never allocates, frees or synchronises
- *     and keeps no mutable global state; scratch memory is the caller's `ws`
- *     buffer of at least moe_workspace_bytes(dims) bytes, which must not be shared
- *     by calls that may run concurrently.
+ *     is the default stream).  The library never allocates, frees or synchronises;
+ *     scratch memory is the caller's `ws` buffer of at least moe_workspace_bytes(dims)
+ *     bytes, which must not be shared by calls that may run concurrently.  The one
+ *     piece of global state is the static device scratch of moe_layer_forward_noalloc
+ *     (and the per-device table of its addresses).
  *   - Arguments are validated on the host before any launch; on error nothing is
  *     launched and a negative moe_status is returned.  T = 0 is a successful no-op.
  *   - Results are deterministic: ids, counts, offsets, permutation are unique
@@ -66,7 +67,8 @@ enum moe_status {
   MOE_ERR_UNSUPPORTED = -3, /* dtype combination, D or I not a multiple of 64, E > 1024, top_k > 32,
                                one expert's or the router's weight matrix of 2 GiB or more */
   MOE_ERR_WORKSPACE = -4,   /* ws_bytes smaller than moe_workspace_bytes(dims) */
-  MOE_ERR_HIP = -5          /* a kernel launch failed (see moe_last_hip_error) */
+  MOE_ERR_HIP = -5,         /* a kernel launch failed (see moe_last_hip_error) */
+  MOE_ERR_SCRATCH_LIMIT = -6 /* moe_layer_forward_noalloc: the dims need more than MOE_STATIC_SCRATCH_BYTES */
 };
 
 /*
@@ -257,6 +259,30 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const vo
                       void* stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Scratch is a static device array of MOE_STATIC_SCRATCH_BYTES inside the library: each
+ * GPU the library runs on holds its own copy until the process ends.  The array's
+ * address on the current device is looked up once per device on the first call; the
+ * call itself allocates nothing and launches the same kernels as moe_layer_forward, so
+ * its results are the same bit for bit.
+ *
+ *   arguments  as for moe_layer_forward, without ws / ws_bytes
+ *   bad_ids    device int32 or NULL: receives the error word (ids outside [0, E) in the
+ *              routing blob), since the static scratch is not visible to the caller
+ * Returns MOE_ERR_SCRATCH_LIMIT (nothing launched) when moe_workspace_bytes(dims)
+ * exceeds MOE_STATIC_SCRATCH_BYTES; the 512-token decode batch of the D = 4096,
+ * E = 512, I = 1024 layer fits, 8192-token prefill batches do not.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind: calls
+ * that may overlap on one GPU (several streams, several host threads) race and must
+ * be serialised by the caller.  Nothing in the array needs to start at zero.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (96u << 20)
+int moe_layer_forward_noalloc(const moe_dims* dims, const moe_weights* weights, const void* x,
+                              const int32_t* packed_in, const float* logit_bias, void* y, float* logits_out,
+                              int32_t* packed_out, int32_t* bad_ids, void* const* stage_events, void* stream);
+
+/*
  * Repack weight matrices from row-major [out][in] into the fragment-major order the
  * grouped GEMM streams: for each block of 16 output rows ("fragment") and each 64-byte
  * slice of the reduction dimension, the 16 x 64 bytes are stored as one contiguous
@@ -326,7 +352,8 @@ const char* moe_status_string(int status);
 int moe_last_hip_error(void);
 
 /* ABI version of this header: 4 (3: MOE_STAGE_EVENTS became 7, with a mark after the shared
- * expert; moe_audit and moe_audit_workspace_bytes were added; 4: the workspace error word). */
+ * expert; moe_audit and moe_audit_workspace_bytes were added; 4: the workspace error word
+ * and moe_layer_forward_noalloc). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,14 +29,15 @@ LAYOUT_ROWS, LAYOUT_PACKED = 0, 1
 _LAYOUT_CODE = {"rows": LAYOUT_ROWS, "packed": LAYOUT_PACKED}
 
 # enum moe_status
-OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_NULL_ARG, ERR_BAD_DIMS, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5, -6
 
 WS_ERROR_OFFSET = 0                     # MOE_WS_ERROR_OFFSET: byte offset of the workspace error word
+STATIC_SCRATCH_BYTES = 96 << 20         # MOE_STATIC_SCRATCH_BYTES
 
 # Symbols exported by the library (the entry points of include/moe.h).
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_route_fused", "moe_permute", "moe_grouped_ffn",
-    "moe_unpermute_combine", "moe_layer_forward", "moe_audit_workspace_bytes", "moe_audit", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
+    "moe_unpermute_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_audit_workspace_bytes", "moe_audit", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
     "moe_abi_version",
 )
 
@@ -88,6 +89,8 @@ def library() -> ctypes.CDLL:
     lib.moe_unpermute_combine.restype = i32
     lib.moe_layer_forward.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.moe_layer_forward.restype = i32
+    lib.moe_layer_forward_noalloc.argtypes = [dp, wp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_layer_forward_noalloc.restype = i32
     lib.moe_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_pack_weights.restype = i32
     lib.moe_audit_workspace_bytes.argtypes = [dp, ctypes.c_int32]
@@ -246,6 +249,29 @@ def moe_layer_forward(dims, weights: moe_weights, x, packed_in, logit_bias, y, l
                                        _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, ev, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(dims, weights: moe_weights, x, packed_in, logit_bias, y, logits_out=None,
+                              packed_out=None, bad_ids=None, stage_events=None, stream=None):
+    """moe_layer_forward on the library's static device scratch (no workspace argument).
+
+    bad_ids: None or a device int32 tensor that receives the count of routing-blob ids outside [0, E).
+    """
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
+        for e in stage_events:
+            if not e.cuda_event:
+                e.record()
+        ev = (ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
+    _check_io(dims, x=x, logits=logits_out, packed=packed_in, bias=logit_bias, y=y)
+    _need(packed_out, dims.T * 2 * dims.top_k * 4, "packed_out")
+    _need(bad_ids, 4, "bad_ids")
+    _check(library().moe_layer_forward_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _ptr(packed_in),
+                                               _ptr(logit_bias), _ptr(y), _ptr(logits_out), _ptr(packed_out),
+                                               _ptr(bad_ids), ev, _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def workspace_error_count(ws: torch.Tensor) -> torch.Tensor:

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe.h"
 #include "common.hpp"
@@ -269,6 +270,30 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
   return MOE_OK;
 }
 
+// Static scratch of moe_layer_forward_noalloc.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels only ever see the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int static_scratch(void** out) {
+  int dev = 0;
+  MOE_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,6 +461,24 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   return hip_status(mark(6));
 }
 
+int moe_layer_forward_noalloc(const moe_dims* dims, const moe_weights* w, const void* x, const int32_t* packed_in,
+                              const float* logit_bias, void* y, float* logits_out, int32_t* packed_out,
+                              int32_t* bad_ids, void* const* stage_events, void* stream) {
+  const int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const size_t need = layout(*dims).total;
+  if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+  if (dims->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int sst = static_scratch(&ws);
+  if (sst != MOE_OK) return sst;
+  const int r = moe_layer_forward(dims, w, x, packed_in, logit_bias, y, logits_out, packed_out, ws,
+                                  MOE_STATIC_SCRATCH_BYTES, stage_events, stream);
+  if (r != MOE_OK || !bad_ids) return r;
+  return hip_status(hipMemcpyAsync(bad_ids, static_cast<uint8_t*>(ws) + MOE_WS_ERROR_OFFSET, sizeof(int32_t),
+                                   hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_audit_workspace_bytes(const moe_dims* dims, int32_t n_sample) {
   if (check_dims(dims) != MOE_OK || n_sample < 1 || n_sample > kAuditMaxSamples) return 0;
   return audit_workspace_bytes(n_sample, dims->top_k, dims->D, std::max(dims->I, dims->I_shared));
@@ -496,6 +539,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported dimensions or dtype combination";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "HIP kernel launch failed";
+    case MOE_ERR_SCRATCH_LIMIT: return "the dims need more scratch than the library's static MOE_STATIC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }

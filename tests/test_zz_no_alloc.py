@@ -1,0 +1,119 @@
+"""moe_layer_forward_noalloc: the layer on the library's static device scratch.
+
+It launches the same kernels as moe_layer_forward, so y, the logits and the
+routing blob must equal those of moe_layer_forward with a caller workspace bit
+for bit, on two calls in a row (the second with a smaller batch, over what the
+first call left in the scratch), and the output also meets the oracle's bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_route_amd as moe
+import synth
+from harness import dims_of, oracle_layer, rel_err, to_np, tolerance
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+# ~60 MB of scratch: the 256-row tile shapes of the grouped GEMMs, near the static limit
+BIG = W("noalloc_big", T=4096, D=1024, E=64, top_k=4, I=512, I_shared=256, act="bf16", w="bf16", out="bf16")
+SMALL = W("noalloc_small", T=300, D=512, E=40, top_k=4, I=192, I_shared=128, act="bf16", w="bf16", out="bf16")
+FP8 = W("noalloc_fp8", T=256, D=512, E=32, top_k=4, I=128, I_shared=0, act="bf16", w="e4m3", out="bf16",
+        expert_begin=8, n_local=8, routing_given=True)
+
+
+def _weights(dev, wl):
+    sh = wl.I_shared > 0
+    return moe.make_weights(dev.w_router, dev.w_gate, dev.w_up, dev.w_down, dev.s_gate, dev.s_up, dev.s_down,
+                            dev.ws_gate if sh else None, dev.ws_up if sh else None, dev.ws_down if sh else None)
+
+
+def _both(dev, wl, packed_in=None):
+    """(moe_layer_forward with a workspace, moe_layer_forward_noalloc) outputs on the same inputs."""
+    d = dims_of(wl)
+    w = _weights(dev, wl)
+    out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
+    res = []
+    for noalloc in (False, True):
+        y = torch.full((wl.T, wl.D), float("nan"), dtype=out_dt, device="cuda")
+        logits = None if wl.routing_given else torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
+        blob = torch.empty(wl.T, 2, wl.top_k, dtype=torch.int32, device="cuda")
+        bad = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        if noalloc:
+            moe.moe_layer_forward_noalloc(d, w, dev.x, packed_in, dev.bias, y, logits, blob, bad)
+        else:
+            ws = moe.workspace(d)
+            moe.moe_layer_forward(d, w, dev.x, packed_in, dev.bias, y, logits, blob, ws)
+            bad = moe.workspace_error_count(ws)
+        torch.cuda.synchronize()
+        res.append(dict(y=y.cpu(), logits=None if logits is None else logits.cpu(), packed=blob.cpu(),
+                        bad=int(bad.cpu()[0])))
+    return res
+
+
+def _same(a, b):
+    assert torch.equal(a["y"].view(torch.int16) if a["y"].dtype == torch.bfloat16 else a["y"],
+                       b["y"].view(torch.int16) if b["y"].dtype == torch.bfloat16 else b["y"])
+    if a["logits"] is not None:
+        assert torch.equal(a["logits"], b["logits"])
+    assert torch.equal(a["packed"], b["packed"])
+    assert a["bad"] == b["bad"]
+
+
+def test_noalloc_matches_workspace_entry_two_calls_second_smaller():
+    print(f"[noalloc] {BIG.name} then {SMALL.name}", flush=True)
+    inp = synth.make_inputs(BIG, 0, "cpu")
+    d = dims_of(BIG)
+    assert moe.moe_workspace_bytes(d) > moe.STATIC_SCRATCH_BYTES // 2      # a large share of the scratch
+    dev = inp.to("cuda")
+    ref, got = _both(dev, BIG)
+    _same(ref, got)
+    assert got["bad"] == 0
+    # second call: a smaller batch of another layer over the scratch the first call left behind
+    inp2 = synth.make_inputs(SMALL, 1, "cpu")
+    dev2 = inp2.to("cuda")
+    ref2, got2 = _both(dev2, SMALL)
+    _same(ref2, got2)
+    orc = oracle_layer(inp2, ref2["logits"].numpy())
+    ids_gpu, w_gpu = oracle.unpack_routing(got2["packed"].numpy())
+    np.testing.assert_array_equal(ids_gpu, orc["ids"])
+    assert rel_err(to_np(got2["y"]), orc["y"]) <= tolerance(SMALL)
+
+
+def test_noalloc_given_blob_counts_out_of_range_ids():
+    print(f"[noalloc] {FP8.name} with junk ids", flush=True)
+    inp = synth.make_inputs(FP8, 2, "cpu")
+    blob = inp.packed.clone()
+    rng = np.random.default_rng(5)
+    ids = blob[:, 0, :].numpy()
+    m = rng.random(ids.shape) < 0.1
+    ids[m] = rng.integers(-3, FP8.E + 3, int(m.sum()))
+    blob[:, 0, :] = torch.from_numpy(ids)
+    n_bad = int(((ids < 0) | (ids >= FP8.E)).sum())
+    assert n_bad > 0
+    dev = inp.to("cuda")
+    dev.packed = blob.cuda()
+    ref, got = _both(dev, FP8, packed_in=dev.packed)
+    _same(ref, got)
+    assert got["bad"] == n_bad
+    # the same call with a clean blob resets the word
+    ref2, got2 = _both(inp.to("cuda"), FP8, packed_in=inp.packed.cuda())
+    _same(ref2, got2)
+    assert got2["bad"] == 0
+
+
+def test_noalloc_rejects_dims_beyond_the_static_scratch():
+    wl = synth.WORKLOADS["prefill_bf16"]
+    d = dims_of(wl)
+    assert moe.moe_workspace_bytes(d) > moe.STATIC_SCRATCH_BYTES
+    lib = moe.library()
+    fake = torch.empty(16, dtype=torch.uint8, device="cuda")
+    w = moe.make_weights(fake, fake, fake, fake)
+    p = moe._ptr(fake)
+    st = lib.moe_layer_forward_noalloc(moe.ctypes.byref(d), moe.ctypes.byref(w), p, None, None, p, None, None, None,
+                                       None, None)
+    assert st == moe.ERR_SCRATCH_LIMIT
