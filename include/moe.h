@@ -250,7 +250,11 @@ int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int3
  *              routing, [1] after routing, [2] after grouping (and the fp8 quantisation
  *              of x), [3] after the routed gate/up GEMM, [4] after the routed down GEMM
  *              (and the fp8 quantisation of h), [5] after the shared expert's two GEMMs,
- *              [6] after the combine.  Only for timing; the kernels are the same either way.
+ *              [6] after the combine.  With a shared expert the combine runs inside the
+ *              shared expert's down projection, so [5] and [6] mark the same point.  Only
+ *              for timing; the kernels are the same either way.
+ * With a shared expert, y[t] = (sum over the slots in order of w * expert row, in fp32)
+ * + the shared expert's fp32 output, rounded once; without one, the slot sum alone.
  */
 #define MOE_STAGE_EVENTS 7
 int moe_layer_forward(const moe_dims* dims, const moe_weights* weights, const void* x,

@@ -83,7 +83,7 @@ int router_splits(const moe_dims& d) {
 
 struct Layout {
   size_t err, logits, logits_part, packed, hist, base, rank, bad, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
-  size_t xq, sx, h, h_sh, hq, sh, out_rows, sh_out, total;
+  size_t xq, sx, h, h_sh, hq, sh, out_rows, total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -120,7 +120,6 @@ Layout layout(const moe_dims& d) {
   L.hq = take(fp8 ? tk * d.I : 0);
   L.sh = take(fp8 ? tk * 4 : 0);
   L.out_rows = take(tk * d.D * os);
-  L.sh_out = take(d.I_shared ? T * d.D * os : 0);
   L.total = off;
   return L;
 }
@@ -170,6 +169,7 @@ GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, in
   p.w0 = w0; p.w1 = w1; p.s0 = s0; p.s1 = s1; p.w_stride = w_stride;
   p.out = out; p.ldo = ldo; p.N = N; p.K = K;
   p.k_splits = 1; p.out_split_stride = 0;
+  p.comb_rows = nullptr; p.comb_packed = nullptr; p.comb_inv = nullptr; p.comb_k = 0;
   return p;
 }
 
@@ -202,13 +202,14 @@ int route_tokens(const moe_dims& d, const void* x, const void* w_router, float* 
 }
 
 // gate/up -> h (+ quantise) -> down for the routed groups, then the optional shared
-// expert in launches of its own.
+// expert in launches of its own, whose down projection also does the unpermute-combine:
+// y[t] = sum_j w[t][j] * out_rows[inv[t][j]] + shared(x_t).
 int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_rows, const float* a_scale,
                     const int32_t* perm, const int32_t* offsets, const void* w_gate, const void* w_up,
                     const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
                     void* out_rows, const void* x_shared, const void* sh_gate, const void* sh_up,
-                    const void* sh_down, void* sh_out, bool have_tile_prefix, hipEvent_t ev_gate_up,
-                    hipEvent_t ev_down, hipStream_t s) {
+                    const void* sh_down, void* y, const int32_t* comb_packed, const int32_t* comb_inv,
+                    bool have_tile_prefix, hipEvent_t ev_gate_up, hipEvent_t ev_down, hipStream_t s) {
   const int shape = expert_shape(d, perm != nullptr);
   const bool packed = d.weight_layout == MOE_LAYOUT_PACKED;
   const int bm = gemm_bm(shape);
@@ -262,10 +263,14 @@ int experts_forward(const moe_dims& d, void* ws, const Layout& L, const void* a_
                                    nullptr, 0, h_sh, d.I_shared, d.I_shared, d.D);
     MOE_TRY(launch_gemm(d.act_dtype, hel, true, sh_shape, packed, gs,
                         ((d.T + sh_bm - 1) / sh_bm) * ((d.I_shared + bn_g - 1) / bn_g), s));
-    const GemmProblem ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr,
-                                   nullptr, nullptr, 0, sh_out, d.D, d.D, d.I_shared);
-    MOE_TRY(launch_gemm(d.act_dtype, oel, false, sh_shape, packed, ds,
-                        ((d.T + sh_bm - 1) / sh_bm) * ((d.D + bn_d - 1) / bn_d), s));
+    GemmProblem ds = problem(h_sh, nullptr, nullptr, d.I_shared, nullptr, nullptr, 1, d.T, sh_down, nullptr,
+                             nullptr, nullptr, 0, y, d.D, d.D, d.I_shared);
+    ds.comb_rows = out_rows;
+    ds.comb_packed = comb_packed;
+    ds.comb_inv = comb_inv;
+    ds.comb_k = d.top_k;
+    MOE_TRY(launch_gemm_combine(d.act_dtype, oel, sh_shape, packed, ds,
+                                ((d.T + sh_bm - 1) / sh_bm) * ((d.D + bn_d - 1) / bn_d), s));
   }
   return MOE_OK;
 }
@@ -376,8 +381,8 @@ int moe_grouped_ffn(const moe_dims* dims, const void* a_rows, const float* a_sca
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
   return experts_forward(d, ws, L, a_rows, a_scale, perm_token, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr, nullptr,
-                         static_cast<hipStream_t>(stream));
+                         out_rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr,
+                         nullptr, static_cast<hipStream_t>(stream));
 }
 
 int moe_unpermute_combine(const moe_dims* dims, const void* out_rows, const int32_t* packed, const int32_t* inv_pos,
@@ -446,18 +451,19 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   }
   MOE_TRY(mark(2));
 
-  // 3. experts (+ shared)
+  // 3. experts; with a shared expert its down projection also does step 4 (the unpermute-
+  // combine) in its epilogue and writes y
   void* out_rows = at<void>(ws, L.out_rows);
-  void* sh_out = d.I_shared ? at<void>(ws, L.sh_out) : nullptr;
+  const bool shared = d.I_shared > 0;
   st = experts_forward(d, ws, L, a_rows, a_scale, perm, offsets, w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up,
-                       w->s_down, out_rows, x, d.I_shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, sh_out, true,
-                       stage_events ? static_cast<hipEvent_t>(stage_events[3]) : nullptr,
+                       w->s_down, out_rows, x, shared ? w->sh_gate : nullptr, w->sh_up, w->sh_down, y, packed, inv,
+                       true, stage_events ? static_cast<hipEvent_t>(stage_events[3]) : nullptr,
                        stage_events ? static_cast<hipEvent_t>(stage_events[4]) : nullptr, s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(5));
 
-  // 4. unpermute + weighted combine (+ shared)
-  MOE_TRY(launch_combine(d.out_dtype, out_rows, packed, inv, sh_out, d.T, d.D, d.top_k, y, s));
+  // 4. unpermute + weighted combine (no shared expert: partial sums of the routed slots only)
+  if (!shared) MOE_TRY(launch_combine(d.out_dtype, out_rows, packed, inv, nullptr, d.T, d.D, d.top_k, y, s));
   return hip_status(mark(6));
 }
 

@@ -89,8 +89,10 @@ struct TileInfo {
   const uint8_t* W1;
 };
 
+// COMB: the epilogue is the fused unpermute-combine of a single-group problem (see
+// GemmProblem::comb_rows), instantiated for the shared expert's down projection only.
 template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED,
-          int TDEPTH>
+          int TDEPTH, bool COMB>
 __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
@@ -206,6 +208,140 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
         OutStore<OUT>::store4(out, static_cast<size_t>(grow) * ldo + n, v, valid);
       }
     }
+  };
+
+  // ---- fused combine epilogue ---------------------------------------------------
+  // In passes of PR rows: the tile's fp32 results are staged in LDS (reusing the token
+  // buffers), and the pass's slot indices and routing weights are loaded into LDS by the
+  // whole workgroup in one coalesced sweep.  Each thread then owns 8 columns of R rows and
+  // issues the loads of all R rows' slots in batches (LOADS 16-byte loads in flight), so a
+  // pass costs a few memory round trips rather than a few per row; every row's sum still
+  // runs over its slots in order: y = sum_j w[t][j] * comb_rows[inv[t][j]] + staged value,
+  // rounded once.
+  auto epilogue_combine = [&](const TileInfo& t, const f32x4 (&acc)[NMAT][NF][MF]) {
+    if constexpr (COMB) {
+      constexpr int SROW = BN + 4;                          // floats per staged row (16-byte pad)
+      constexpr int KMAX = 32;                              // largest top_k the library accepts
+      constexpr int LDS_BYTES = 2 * BM * LDS_ROW;
+      constexpr int ROW_BYTES = SROW * 4 + KMAX * 8;        // staged row + its slot indices and weights
+      constexpr int PR1 = (LDS_BYTES / ROW_BYTES) / 16 * 16;
+      constexpr int PR2 = PR1 < BM ? PR1 : BM;
+      constexpr int PR = PR2 >= 64 && BM % 64 == 0 ? 64 : PR2 >= 32 && BM % 32 == 0 ? 32 : 16;  // rows per pass
+      static_assert(PR * ROW_BYTES <= LDS_BYTES && BM % PR == 0, "combine staging pass must fit the LDS");
+      constexpr int TPR = BN / 8;                           // threads per row (8 columns each)
+      constexpr int RPI = 256 / TPR;                        // rows per workgroup sweep
+      constexpr int R = PR / RPI;                           // rows per thread per pass
+      static_assert(R >= 1 && PR % RPI == 0, "rows per pass must split evenly over the threads");
+      constexpr int PIECES = OUT == EL_F32 ? 2 : 1;         // 16-byte loads per 8-column piece
+      constexpr int LOADS = 20 / PIECES;                    // pieces in flight per thread
+      constexpr int KB = LOADS / R > 0 ? LOADS / R : 1;     // slots per batch
+      float* st = reinterpret_cast<float*>(&sA[0][0]);
+      int32_t* s_inv = reinterpret_cast<int32_t*>(st + PR * SROW);
+      float* s_w = reinterpret_cast<float*>(s_inv + PR * KMAX);
+      const int N = t.N, k = p.comb_k;
+      const int cw = wave * NF * 16;
+      const int cc = (threadIdx.x % TPR) * 8;
+      const int n = t.n_tile * BN + cc;
+      const int r0 = threadIdx.x / TPR;
+      const size_t ldo = p.ldo;
+      typedef typename std::conditional<OUT == EL_F32, float, uint16_t>::type OutT;
+      const OutT* rows_src = static_cast<const OutT*>(p.comb_rows);
+      OutT* out = static_cast<OutT*>(p.out);
+#pragma unroll
+      for (int pass = 0; pass < BM / PR; ++pass) {
+        __syncthreads();  // the K loop's last LDS reads (or the previous pass) are done
+#pragma unroll
+        for (int m = 0; m < PR / 16; ++m) {
+          const int mf = pass * (PR / 16) + m;
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            *reinterpret_cast<f32x4*>(&st[(m * 16 + lrow) * SROW + cw + nf * 16 + lgrp * 4]) = acc[0][nf][mf];
+        }
+        // the pass's rows are tokens tok0 .. tok0 + rows - 1: their k slot indices are one
+        // contiguous run of inv, their weights plane 1 of each token's blob
+        const int rows = min(PR, t.nrows - pass * PR);
+        const int tok0 = t.row0 + t.rbeg + pass * PR;
+        for (int q = threadIdx.x; q < rows * k; q += 256) {
+          const int r = q / k, j = q - r * k;
+          s_inv[r * KMAX + j] = p.comb_inv[static_cast<size_t>(tok0) * k + q];
+          s_w[r * KMAX + j] = __int_as_float(p.comb_packed[(static_cast<size_t>(tok0) + r) * 2 * k + k + j]);
+        }
+        __syncthreads();
+        if (n < N && r0 < rows) {
+          float a[R][8];
+#pragma unroll
+          for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) a[i][q] = 0.f;
+          for (int j0 = 0; j0 < k; j0 += KB) {
+            int ri[R][KB];
+            u32x4 v[R][KB][PIECES];
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+              for (int u = 0; u < KB; ++u) {
+                const int rr = r0 + i * RPI;
+                ri[i][u] = (rr < rows && j0 + u < k) ? s_inv[rr * KMAX + j0 + u] : -1;
+              }
+            // Unconditional loads: a missing slot (not local, or past k) reads row 0, which is
+            // never summed.  With the loads under per-slot branches the compiler waited for each
+            // load before issuing the next.
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+              for (int u = 0; u < KB; ++u) {
+                const OutT* src = rows_src + static_cast<size_t>(ri[i][u] < 0 ? 0 : ri[i][u]) * ldo + n;
+#pragma unroll
+                for (int c = 0; c < PIECES; ++c) v[i][u][c] = reinterpret_cast<const u32x4*>(src)[c];
+              }
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+              for (int u = 0; u < KB; ++u) {
+                if (ri[i][u] < 0) continue;
+                const float w = s_w[(r0 + i * RPI) * KMAX + j0 + u];
+                float x[8];
+                if constexpr (OUT == EL_F32) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) {
+                    x[q] = __uint_as_float(v[i][u][0][q]);
+                    x[4 + q] = __uint_as_float(v[i][u][PIECES - 1][q]);
+                  }
+                } else {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) {
+                    x[2 * q] = bf16_bits_to_f32(v[i][u][0][q] & 0xFFFFu);
+                    x[2 * q + 1] = bf16_bits_to_f32(v[i][u][0][q] >> 16);
+                  }
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) a[i][q] = fmaf(w, x[q], a[i][q]);
+              }
+          }
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const int rr = r0 + i * RPI;
+            if (rr >= rows) break;
+            const float* sv = &st[rr * SROW + cc];
+            float o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = a[i][q] + sv[q];
+            OutT* dst = out + static_cast<size_t>(tok0 + rr) * ldo + n;
+            if constexpr (OUT == EL_F32) {
+              reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+              reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+            } else {
+              *reinterpret_cast<uint4*>(dst) = make_uint4(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]),
+                                                          bf16x2_bits(o[4], o[5]), bf16x2_bits(o[6], o[7]));
+            }
+          }
+        }
+      }
+    }
+  };
+  auto finish = [&](const TileInfo& t, const f32x4 (&acc)[NMAT][NF][MF]) {
+    if constexpr (COMB) epilogue_combine(t, acc);
+    else epilogue(t, acc);
   };
 
   if constexpr (MF >= 8) {
@@ -404,7 +540,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
         __syncthreads();
         mm(wr[0], buf, tail_steps);
       }
-      epilogue(ti, acc);
+      finish(ti, acc);
     };
     static_assert(MF % kFragGroup == 0, "tile height must be whole fragment groups");
     switch ((mf_active + kFragGroup - 1) / kFragGroup) {
@@ -608,7 +744,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
           if (s < tail_steps) step(wb[0], buf, s);
       }
     }
-    epilogue(ti, acc);
+    finish(ti, acc);
   }
 }
 
@@ -642,14 +778,24 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIG
   static constexpr bool NT = PACKED;
 };
 
-template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED>
+template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED, bool COMB = false>
 hipError_t launch_one(const GemmProblem& p, int max_tiles, hipStream_t stream) {
   using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
   constexpr int NF = gemm_nf(SWIGLU, SHAPE, EL, PACKED);
   if (max_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH>),
-                     dim3(max_tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(
+      (gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH, COMB>),
+      dim3(max_tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int EL, int OUT>
+hipError_t launch_combine_shapes(int shape, bool packed, const GemmProblem& p, int max_tiles, hipStream_t stream) {
+  if (shape == kShapeTile256)
+    return packed ? launch_one<EL, OUT, false, kShapeTile256, true, true>(p, max_tiles, stream)
+                  : launch_one<EL, OUT, false, kShapeTile256, false, true>(p, max_tiles, stream);
+  return packed ? launch_one<EL, OUT, false, kShapeStream32, true, true>(p, max_tiles, stream)
+                : launch_one<EL, OUT, false, kShapeStream32, false, true>(p, max_tiles, stream);
 }
 
 template <int EL, int OUT, bool SWIGLU, bool PACKED>
@@ -685,6 +831,19 @@ hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, 
     if (el == EL_E4M3 && out_el == EL_F32) MOE_GEMM(EL_E4M3, EL_F32, false);
   }
 #undef MOE_GEMM
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_combine(int el, int out_el, int shape, bool packed, const GemmProblem& p, int max_tiles,
+                               hipStream_t stream) {
+  if (!p.comb_rows || !p.comb_packed || !p.comb_inv || p.offsets || p.perm || p.k_splits != 1)
+    return hipErrorInvalidValue;
+  if (shape != kShapeTile256 && shape != kShapeStream32) return hipErrorInvalidValue;
+  if (el == EL_F32 && out_el == EL_F32) return launch_combine_shapes<EL_F32, EL_F32>(shape, packed, p, max_tiles, stream);
+  if (el == EL_BF16 && out_el == EL_BF16)
+    return launch_combine_shapes<EL_BF16, EL_BF16>(shape, packed, p, max_tiles, stream);
+  if (el == EL_BF16 && out_el == EL_F32)
+    return launch_combine_shapes<EL_BF16, EL_F32>(shape, packed, p, max_tiles, stream);
   return hipErrorInvalidValue;
 }
 

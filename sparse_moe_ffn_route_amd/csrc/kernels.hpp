@@ -34,6 +34,14 @@ struct GemmProblem {
   int N, K;
   int k_splits;                // single-group problems only: K is cut into k_splits equal ranges,
   long long out_split_stride;  // each writing its partial product at out + split * out_split_stride
+  // Fused unpermute-combine (single-group, non-SwiGLU problems: the shared expert's down
+  // projection).  With comb_rows set, out row t is
+  //   sum_j w[t][j] * comb_rows[inv[t][j]]  (slot order, inv < 0 skipped)  +  (A W0^T)[t]
+  // in fp32, rounded once; comb_rows is [*][ldo] of the output type.
+  const void* comb_rows;
+  const int32_t* comb_packed;  // [rows][2][comb_k] routing blob (weights from plane 1)
+  const int32_t* comb_inv;     // [rows][comb_k] grouped row of each slot, or -1
+  int comb_k;
 };
 
 // Launch shapes of the grouped GEMM (see gemm.hip):
@@ -120,6 +128,12 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int
 //   max_tiles: host upper bound of the problem's tiles (the grid; surplus workgroups exit).
 hipError_t launch_gemm(int el, int out_el, bool swiglu, int shape, bool packed, const GemmProblem& p, int max_tiles,
                        hipStream_t stream);
+
+// The same GEMM with the fused combine epilogue (p.comb_* set; no SwiGLU): el and out_el
+// EL_F32 / EL_F32 or EL_BF16 / EL_BF16 or EL_BF16 / EL_F32, shape kShapeStream32 or
+// kShapeTile256.
+hipError_t launch_gemm_combine(int el, int out_el, int shape, bool packed, const GemmProblem& p, int max_tiles,
+                               hipStream_t stream);
 
 // Repack n_mats row-major [rows][row_bytes] matrices into the fragment-major layout.
 // Streaming read of bytes (multiple of 16) at src; sink receives one word per workgroup
