@@ -177,12 +177,13 @@ def layer_summary(layer, wall, stages, steps):
                 layer_roofline_frac=max(hbm_frac, mfma_frac), stage_ms=stages, work=w)
 
 
-def roofline_of(layer, stages):
+def roofline_of(layer, stages, summary=None):
     w = layer.work()
     t = stages["gate_up"] * 1e-3
     achieved = w["gate_up_bytes"] / t / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(layer.wl.name),
+            "layer_frac": None if summary is None else round(summary["layer_roofline_frac"], 4),
             "kernel": f"gemm_kernel<{layer.wl.w},SwiGLU> (routed grouped gate/up)",
             "bytes_per_launch": w["gate_up_bytes"], "avg_launch_ms": round(stages["gate_up"], 4),
             "mfma_TFLOPs": round(w["gate_up_flop"] / t / 1e12, 1)}
@@ -225,7 +226,7 @@ def cpu_baseline(layer, sample_tokens):
             oracle.layer_from_routing(x64, ids, w, synth.ExpertView(host), shared=synth.shared_f64(host),
                                       expert_begin=wl.expert_begin, n_local=wl.local)
         dt = time.perf_counter() - t0
-    return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {T} tokens of the {wl.name} batch (T={wl.T}): fp64 NumPy oracle, routing from the "
                       f"GPU's fp32 logits, grouped experts, combine; {dt:.1f} s",
             "seconds": round(dt, 2)}
@@ -272,7 +273,7 @@ def router_variants(wl, x, w_router, reps=20):
     logits = torch.empty(T, wl.E, dtype=torch.float32, device="cuda")
     packed = torch.empty(T, 2, wl.top_k, dtype=torch.int32, device="cuda")
     calls = {"two_kernel_us": lambda: moe.moe_route(d, x, w_router, logits, None, packed, ws=ws),
-             "fused_us": lambda: moe.moe_route_fused(d, x, w_router, None, None, packed)}
+             "fused_us": lambda: moe.moe_route_fused(d, x, w_router, None, None, packed, ws=ws)}
     out = {}
     for name, fn in calls.items():
         for _ in range(3):
@@ -303,6 +304,32 @@ def hbm_probe(buf, reps=5):
         torch.cuda.synchronize()
         best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     return round(best, 1)
+
+
+def mfma_probe(dtype, iters=4000, reps=3):
+    """Best-of-reps dense MFMA rate (TFLOP/s) of moe_mfma_peak_probe: register-only MFMA chains on every CU."""
+    import torch
+    import sparse_moe_ffn_route_amd as moe
+    sink = torch.empty(moe.MFMA_PROBE_BLOCKS, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, flop = moe.moe_mfma_peak_probe(dtype, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -360,7 +387,7 @@ def main():
         layer2 = Layer(wl2, inp2, pw2)
         wall2, stages2 = layer2.run(args.secondary_steps, 2)
         sec = layer_summary(layer2, wall2, stages2, args.secondary_steps)
-        sec["roofline"] = roofline_of(layer2, stages2)
+        sec["roofline"] = roofline_of(layer2, stages2, sec)
         if wl2.w == "e4m3":
             sec["audit"] = audit_of(layer2)
         secondary.append(sec)
@@ -381,8 +408,12 @@ def main():
     measured = None
     if not args.no_hbm_probe:
         measured = {"hbm_read_GBs": hbm_probe(packed_w["w_gate"] if packed_w else inp.w_gate),
-                    "how": "moe_hbm_read_probe over the expert gate weights (non-temporal 16-byte loads), best of 5"}
-        print(f"[bench] streaming read: {measured['hbm_read_GBs']} GB/s", file=sys.stderr, flush=True)
+                    "how": "moe_hbm_read_probe over the expert gate weights (non-temporal 16-byte loads), best of 5",
+                    "mfma_bf16_TFLOPs": mfma_probe("bf16"), "mfma_fp8_TFLOPs": mfma_probe("e4m3"),
+                    "mfma_how": "moe_mfma_peak_probe: 2048 workgroups x 4 waves x 8 independent MFMA chains on "
+                                "register operands (bf16 16x16x32, e4m3 16x16x128), best of 3"}
+        print(f"[bench] streaming read: {measured['hbm_read_GBs']} GB/s, MFMA bf16 {measured['mfma_bf16_TFLOPs']} "
+              f"fp8 {measured['mfma_fp8_TFLOPs']} TFLOP/s", file=sys.stderr, flush=True)
 
     probe = copy_probe(args.copy_probe_mib) if args.copy_probe_mib else None
 
@@ -408,7 +439,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "D": wl.D, "E": wl.E, "top_k": wl.top_k, "I": wl.I,
                    "I_shared": wl.I_shared, "expert_slice": [wl.expert_begin, wl.local],
                    "weight_layout": args.layout, "parallelism": "1 GPU"},
-        "roofline": roofline_of(layer, stages),
+        "roofline": roofline_of(layer, stages, prim),
         "cpu_baseline": cpu,
         "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_roofline_frac", "stage_ms",
                                         "step_ms_events")},
@@ -422,6 +453,10 @@ def main():
     if measured:
         out["measured_peaks"] = measured
         out["roofline"]["frac_of_measured_hbm"] = round(out["roofline"]["achieved"] / measured["hbm_read_GBs"], 4)
+        for sec in secondary:
+            sec["roofline"]["frac_of_measured_hbm"] = round(sec["roofline"]["achieved"] / measured["hbm_read_GBs"], 4)
+            peak = measured["mfma_fp8_TFLOPs"] if sec["workload"].endswith("fp8") else measured["mfma_bf16_TFLOPs"]
+            sec["roofline"]["mfma_frac_of_measured"] = round(sec["roofline"]["mfma_TFLOPs"] / peak, 4)
     if probe:
         out["copy_probe"] = probe
     print(json.dumps(out))

@@ -150,21 +150,24 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* 
               const float* logit_bias, int32_t* packed, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The same routing as moe_route with x and w_router given, computed by one fused kernel:
- * the projection, the top-k selection, the weights and the packed blob per block of 64
- * tokens, so the fp32 logits stay on chip unless `logits` asks for a copy.  Fusing the
- * selection into the kernel that produces the logits is the open item of Playbook
- * "The Remaining Roadmap".  Opt-in: every workgroup streams all of w_router, which on
- * MI355X is slower than moe_route's projection spread over the whole chip.
+ * The same routing as moe_route with x and w_router given, with the top-k selection
+ * fused into the kernel that produces the logits (the open item of Playbook "The
+ * Remaining Roadmap"): each workgroup computes the logits of a block of tokens against a
+ * slice of 64 (or, above 2048 tokens, 128) experts with MFMAs in fp32 and keeps each
+ * token's top_k of that slice as candidates (key, id); a second kernel merges every
+ * token's candidates of all slices into its top_k with the same order, which is exact
+ * because the global top_k lies in the union of the slices' top_k.  The fp32 logits never
+ * go to memory unless `logits` asks for a copy.
  *
  *   x, w_router, logit_bias, packed   as for moe_route (x and w_router required)
  *   logits     [T][E] fp32 output copy of the logits, or NULL for none
- * Needs E <= 512 and x, w_router each below 2 GiB, else MOE_ERR_UNSUPPORTED.  The ids
- * and weights equal moe_route's for the same fp32 logits; the logits themselves may
- * differ by summation order (both within the fp32 accumulation bound).  No workspace.
+ *   ws         scratch of ws_bytes >= moe_workspace_bytes(dims) (the candidates)
+ * Needs x and w_router each below 2 GiB, else MOE_ERR_UNSUPPORTED.  The ids and weights
+ * equal moe_route's for the same fp32 logits; the logits themselves may differ by
+ * summation order (both within the fp32 accumulation bound).
  */
 int moe_route_fused(const moe_dims* dims, const void* x, const void* w_router, float* logits,
-                    const float* logit_bias, int32_t* packed, void* stream);
+                    const float* logit_bias, int32_t* packed, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Permutation: group the (token, slot) pairs whose expert is local by expert
@@ -349,6 +352,20 @@ int moe_audit(const moe_dims* dims, const moe_weights* weights, const void* x, c
  */
 int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Measurement helper, not part of the layer: the matrix cores' sustained rate.  Launches
+ * MOE_MFMA_PROBE_BLOCKS workgroups of 4 waves; each wave runs iters rounds of 8
+ * independent MFMA accumulator chains on register operands (no memory traffic in the
+ * loop): dtype MOE_BF16 issues 16x16x32 bf16 MFMAs (16384 FLOP each), MOE_E4M3 16x16x128
+ * E4M3 MFMAs (65536 FLOP each).  FLOP per launch = MOE_MFMA_PROBE_BLOCKS * 4 * 8 * iters *
+ * (FLOP per MFMA); timing a launch of a few milliseconds gives the dense MFMA rate at the
+ * clock the chip holds under that load, which the grouped GEMMs are compared with.  sink:
+ * device, at least MOE_MFMA_PROBE_BLOCKS floats (one sum per workgroup).  Asynchronous on
+ * stream.  MOE_ERR_UNSUPPORTED for another dtype, MOE_ERR_BAD_DIMS for iters < 1.
+ */
+#define MOE_MFMA_PROBE_BLOCKS 2048
+int moe_mfma_peak_probe(int32_t dtype, int32_t iters, float* sink, void* stream);
+
 /* Human-readable text of a moe_status code (static storage). */
 const char* moe_status_string(int status);
 
@@ -356,8 +373,8 @@ const char* moe_status_string(int status);
 int moe_last_hip_error(void);
 
 /* ABI version of this header: 4 (3: MOE_STAGE_EVENTS became 7, with a mark after the shared
- * expert; moe_audit and moe_audit_workspace_bytes were added; 4: the workspace error word
- * and moe_layer_forward_noalloc). */
+ * expert; moe_audit and moe_audit_workspace_bytes were added; 4: the workspace error word,
+ * moe_layer_forward_noalloc and moe_mfma_peak_probe). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ STATIC_SCRATCH_BYTES = 96 << 20         # MOE_STATIC_SCRATCH_BYTES
 EXPORTS = (
     "moe_workspace_bytes", "moe_route", "moe_route_fused", "moe_permute", "moe_grouped_ffn",
     "moe_unpermute_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_audit_workspace_bytes", "moe_audit", "moe_pack_weights", "moe_hbm_read_probe", "moe_status_string", "moe_last_hip_error",
-    "moe_abi_version",
+    "moe_abi_version", "moe_mfma_peak_probe",
 )
 
 
@@ -79,7 +79,7 @@ def library() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
-    lib.moe_route_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_route_fused.restype = i32
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
@@ -99,6 +99,8 @@ def library() -> ctypes.CDLL:
     lib.moe_audit.restype = i32
     lib.moe_hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.moe_hbm_read_probe.restype = i32
+    lib.moe_mfma_peak_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.moe_mfma_peak_probe.restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_hip_error.argtypes = []
@@ -184,11 +186,13 @@ def moe_route(dims, x, w_router, logits, logit_bias, packed, ws=None, stream=Non
            "moe_route")
 
 
-def moe_route_fused(dims, x, w_router, logits, logit_bias, packed, stream=None):
+def moe_route_fused(dims, x, w_router, logits, logit_bias, packed, ws=None, stream=None):
     """Fused projection + top-k + blob (logits: optional fp32 copy, or None)."""
     _check_io(dims, x=x, logits=logits, packed=packed, bias=logit_bias, w_router=w_router)
+    if ws is None:
+        ws = workspace(dims, device=x.device)
     _check(library().moe_route_fused(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(logit_bias),
-                                     _ptr(packed), _stream(stream)), "moe_route_fused")
+                                     _ptr(packed), _ptr(ws), ws.numel(), _stream(stream)), "moe_route_fused")
 
 
 def moe_permute(dims, packed, counts, offsets, perm_token, inv_pos, x=None, x_perm=None, x_perm_scale=None,
@@ -328,6 +332,20 @@ def moe_hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, s
     _check(library().moe_hbm_read_probe(_ptr(buf), nbytes - nbytes % 16, _ptr(sink), _stream(stream)),
            "moe_hbm_read_probe")
     return sink
+
+
+MFMA_PROBE_BLOCKS = 2048   # MOE_MFMA_PROBE_BLOCKS
+_MFMA_PROBE_FLOP = {BF16: 16384, E4M3: 65536}
+
+
+def moe_mfma_peak_probe(dtype: str, iters: int, sink: Optional[torch.Tensor] = None, stream=None):
+    """Launch the MFMA throughput probe; returns (sink tensor, FLOP of the launch)."""
+    code = _DTYPE_CODE[dtype]
+    if sink is None:
+        sink = torch.empty(MFMA_PROBE_BLOCKS, dtype=torch.float32, device="cuda")
+    _need(sink, MFMA_PROBE_BLOCKS * 4, "sink")
+    _check(library().moe_mfma_peak_probe(code, iters, _ptr(sink), _stream(stream)), "moe_mfma_peak_probe")
+    return sink, MFMA_PROBE_BLOCKS * 4 * 8 * iters * _MFMA_PROBE_FLOP.get(code, 0)
 
 
 def torch_dtype(code: int) -> torch.dtype:

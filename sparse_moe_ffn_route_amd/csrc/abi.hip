@@ -83,6 +83,7 @@ int router_splits(const moe_dims& d) {
 
 struct Layout {
   size_t err, logits, logits_part, packed, hist, base, rank, bad, counts, offsets, tp_a, tp_b, perm_token, inv_pos;
+  size_t cand_key, cand_id, cand_stats;
   size_t xq, sx, h, h_sh, hq, sh, out_rows, total;
 };
 
@@ -103,6 +104,10 @@ Layout layout(const moe_dims& d) {
   const int rs = router_splits(d);
   L.logits_part = take(rs > 1 ? static_cast<size_t>(rs) * T * d.E * 4 : 0);
   L.packed = take(tk * 2 * 4);
+  const size_t ns = router_fused_slices(d.T, d.E);
+  L.cand_key = take(T * ns * d.top_k * 4);
+  L.cand_id = take(T * ns * d.top_k * 4);
+  L.cand_stats = take(T * ns * 8);
   L.hist = take(nl * U * 4);
   L.base = take(nl * U * 4);
   L.rank = take(tk * 4);
@@ -173,14 +178,18 @@ GemmProblem problem(const void* a, const int32_t* perm, const float* a_scale, in
   return p;
 }
 
-// The fused router kernel (projection, top-k and blob in one launch) serves E <= 512
-// when x and W_r fit its 32-bit offsets.  It is an opt-in entry point: each 64-token
-// workgroup streams all of W_r, which measured slower on MI355X than the GEMM split
-// over the whole chip followed by the route kernel.
+// The fused router (projection and per-slice top-k, then an exact merge) addresses x and
+// W_r with 32-bit offsets.
 bool fused_router_fits(const moe_dims& d) {
   const int64_t es = act_size(d.act_dtype);
-  return d.E <= kMaxFusedExperts && static_cast<int64_t>(d.T) * d.D * es < (1ll << 31) &&
-         static_cast<int64_t>(d.E) * d.D * es < (1ll << 31);
+  return static_cast<int64_t>(d.T) * d.D * es < (1ll << 31) && static_cast<int64_t>(d.E) * d.D * es < (1ll << 31);
+}
+
+int route_fused(const moe_dims& d, const Layout& L, void* ws, const void* x, const void* w_router, float* logits,
+                const float* bias, int32_t* packed, hipStream_t s) {
+  return hip_status(launch_router_topk(d.act_dtype, x, w_router, bias, d.T, d.D, d.E, d.top_k, d.renormalize, logits,
+                                       packed, at<float>(ws, L.cand_key), at<int32_t>(ws, L.cand_id),
+                                       at<float2>(ws, L.cand_stats), s));
 }
 
 // Router projection + top-k.  parts: scratch for split-K partial products (NULL: no split).
@@ -323,15 +332,16 @@ int moe_route(const moe_dims* dims, const void* x, const void* w_router, float* 
 }
 
 int moe_route_fused(const moe_dims* dims, const void* x, const void* w_router, float* logits, const float* logit_bias,
-                    int32_t* packed, void* stream) {
+                    int32_t* packed, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims& d = *dims;
-  if (!x || !w_router || !packed) return MOE_ERR_NULL_ARG;
+  if (!x || !w_router || !packed || !ws) return MOE_ERR_NULL_ARG;
   if (!fused_router_fits(d)) return MOE_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d.T == 0) return MOE_OK;
-  return hip_status(launch_router_topk(d.act_dtype, x, w_router, logit_bias, d.T, d.D, d.E, d.top_k, d.renormalize,
-                                       logits, packed, static_cast<hipStream_t>(stream)));
+  return route_fused(d, L, ws, x, w_router, logits, logit_bias, packed, static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, int32_t* offsets, int32_t* perm_token,
@@ -535,6 +545,13 @@ int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stre
   if (bytes == 0) return MOE_OK;
   if (!buf || !sink) return MOE_ERR_NULL_ARG;
   return hip_status(launch_read_probe(buf, static_cast<int64_t>(bytes), sink, static_cast<hipStream_t>(stream)));
+}
+
+int moe_mfma_peak_probe(int32_t dtype, int32_t iters, float* sink, void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (iters < 1) return MOE_ERR_BAD_DIMS;
+  if (!sink) return MOE_ERR_NULL_ARG;
+  return hip_status(launch_mfma_probe(dtype, iters, sink, static_cast<hipStream_t>(stream)));
 }
 
 const char* moe_status_string(int status) {

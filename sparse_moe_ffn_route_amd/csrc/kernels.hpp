@@ -89,11 +89,16 @@ constexpr int kAuditMaxWidth = 16384;  // D and I limits (one fp32 vector in LDS
 size_t audit_workspace_bytes(int n_sample, int k, int D, int i_max);
 hipError_t launch_audit(const AuditLaunch& l, hipStream_t stream);
 
-// Fused router projection + top-k for E <= kMaxFusedExperts (act: bf16 or fp32 codes of
-// EL_*): 64 tokens per workgroup; logits_out (nullable) receives the fp32 logits.
-constexpr int kMaxFusedExperts = 512;
+// Fused router projection + top-k (act: bf16 or fp32 codes of EL_*): per (token block,
+// expert slice) top-k candidates, then an exact merge per token.  logits_out (nullable)
+// receives the fp32 logits.  Scratch: cand_key / cand_id [T][n_slices][k], stats
+// [T][n_slices] with n_slices = router_fused_slices(T, E).
+constexpr int kFusedSmallT = 2048;          // up to this many tokens: 16-token blocks, 64-expert slices
+constexpr int kMaxFusedCandidates = 512;    // slices (E / 64 <= 16) x top_k (<= 32)
+int router_fused_slices(int T, int E);
 hipError_t launch_router_topk(int el, const void* x, const void* w_router, const float* bias, int T, int D, int E,
-                              int k, int renormalize, float* logits_out, int32_t* packed, hipStream_t stream);
+                              int k, int renormalize, float* logits_out, int32_t* packed, float* cand_key,
+                              int32_t* cand_id, float2* stats, hipStream_t stream);
 
 // Top-k routing.  When n_parts > 1, the logits are the sum of n_parts partial products
 // parts[p][T][E] (added in order p = 0, 1, ...), written to `logits` before routing.
@@ -140,6 +145,11 @@ hipError_t launch_gemm_combine(int el, int out_el, int shape, bool packed, const
 // (at most kReadProbeBlocks workgroups).
 constexpr int kReadProbeBlocks = 16384;
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+// MFMA throughput probe: kMfmaProbeBlocks workgroups of 4 waves, each wave iters x 8 MFMAs
+// (bf16 16x16x32 or E4M3 16x16x128); sink receives one float per workgroup.
+constexpr int kMfmaProbeBlocks = 2048;
+hipError_t launch_mfma_probe(int el, int iters, float* sink, hipStream_t stream);
 
 hipError_t launch_pack(const void* src, void* dst, int64_t n_mats, int rows, int row_bytes, hipStream_t stream);
 

@@ -64,7 +64,48 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
   if (threadIdx.x == 0) sink[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
 }
 
+// MFMA throughput probe: each wave runs `iters` rounds of kProbeChains independent
+// accumulator chains, one MFMA per chain per round, on operands held in registers (no
+// memory traffic in the loop), so the launch time measures the matrix cores' sustained
+// rate at the clock the chip holds under that load.  bf16: 16x16x32 (16384 FLOP per
+// MFMA); E4M3: 16x16x128 of the f8f6f4 family (65536 FLOP).  Lane 0 of each workgroup
+// writes the sum of its accumulators to sink, so the work cannot be dropped.
+constexpr int kProbeChains = 8;
+
+template <int EL>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
+  // small finite operands (bf16 1/128 pairs; E4M3 1.0) that differ per lane
+  const uint32_t base = EL == EL_E4M3 ? 0x38383838u : 0x3C003C00u;
+  const uint32_t t = threadIdx.x & 3;
+  const u32x4 a = {base, base ^ (t << 8), base, base ^ t};
+  const u32x4 b = {base ^ t, base, base ^ (t << 8), base};
+  f32x4 acc[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kProbeChains; ++c) {
+      if constexpr (EL == EL_E4M3)
+        acc[c] = mfma_e4m3_pair(a, b, b, a, acc[c]);
+      else
+        acc[c] = mfma_chunk<EL_BF16>(a, b, acc[c]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (threadIdx.x == 0) sink[blockIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(int el, int iters, float* sink, hipStream_t stream) {
+  if (el == EL_E4M3)
+    hipLaunchKernelGGL(mfma_probe_kernel<EL_E4M3>, dim3(kMfmaProbeBlocks), dim3(256), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel<EL_BF16>, dim3(kMfmaProbeBlocks), dim3(256), 0, stream, iters, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t n16 = bytes / 16;

@@ -174,6 +174,16 @@ def test_hbm_read_probe_reads_every_byte_once():
     assert got == np.bitwise_xor.reduce(words)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_mfma_peak_probe_runs(dtype):
+    """The MFMA probe completes and leaves finite, non-zero sums (its work was not dropped)."""
+    sink, flop = moe.moe_mfma_peak_probe(dtype, 64)
+    torch.cuda.synchronize()
+    s = sink.cpu().numpy()
+    assert flop == moe.MFMA_PROBE_BLOCKS * 4 * 8 * 64 * (16384 if dtype == "bf16" else 65536)
+    assert np.isfinite(s).all() and (s != 0).all()
+
+
 def test_pack_weights_layout():
     """moe_pack_weights places row (16 f + l % 16), bytes [64 s + 16 (l / 16), +16) at run (f, s), chunk l."""
     rng = np.random.default_rng(3)
@@ -302,10 +312,13 @@ def test_route_with_router_projection_bf16(split, T, D, E, k):
 
 
 @pytest.mark.parametrize("T,D,E,k,act,renorm,biased", [
-    (333, 512, 128, 6, "bf16", True, False),     # ragged last 64-token block, E below 512
-    (3000, 512, 200, 8, "bf16", True, True),     # bias, E not a multiple of 64
-    (100, 256, 64, 4, "f32", False, False),      # fp32 operands, no renormalisation
+    (333, 512, 128, 6, "bf16", True, False),     # ragged last 16-token block, two 64-expert slices
+    (3000, 512, 200, 8, "bf16", True, True),     # 64-token blocks, 128-expert slices, bias, E not a multiple of 64
+    (100, 256, 64, 4, "f32", False, False),      # fp32 operands, no renormalisation (slice softmax sums)
+    (2500, 256, 300, 12, "bf16", False, True),   # no renormalisation with bias over three 128-expert slices
     (512, 4096, 512, 10, "bf16", True, False),   # the decode router shape
+    (77, 128, 1024, 32, "bf16", True, False),    # the largest E and k: 16 slices x 32 candidates per token
+    (40, 128, 80, 32, "bf16", True, True),       # a slice with fewer experts than k (sentinel candidates)
 ])
 def test_route_fused_matches_definition(T, D, E, k, act, renorm, biased):
     """The fused router: logits within the fp32 bound, routing bit-exact from its own logits,

@@ -84,6 +84,14 @@ def test_hbm_read_probe_argument_checks():
     assert lib.moe_hbm_read_probe(None, 0, None, None) == moe.OK                  # nothing to read
 
 
+def test_mfma_peak_probe_argument_checks():
+    lib = moe.library()
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_mfma_peak_probe(moe.F32, 10, fake, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_mfma_peak_probe(moe.BF16, 0, fake, None) == moe.ERR_BAD_DIMS
+    assert lib.moe_mfma_peak_probe(moe.E4M3, 10, None, None) == moe.ERR_NULL_ARG
+
+
 UNSUPPORTED = [dict(D=96), dict(I=100), dict(I_shared=32), dict(E=2048, top_k=2), dict(E=64, top_k=33),
                dict(act="f32", w="bf16"), dict(act="f32", w="f32", out="bf16"), dict(act="bf16", w="f32"),
                dict(act="e4m3", w="e4m3"),
@@ -182,13 +190,17 @@ def test_binding_refuses_tensors_smaller_than_the_dims():
 def test_fused_router_argument_checks():
     lib = moe.library()
     fake = ctypes.c_void_p(256)
-    big_e = moe.make_dims(64, 256, 1024, 4, 64)
-    assert lib.moe_route_fused(ctypes.byref(big_e), fake, fake, None, None, fake, None) == moe.ERR_UNSUPPORTED
+    big_x = moe.make_dims(65536, 16384, 16, 4, 64)              # x of 2 GiB: past the 32-bit offsets
+    n = moe.moe_workspace_bytes(big_x)
+    assert lib.moe_route_fused(ctypes.byref(big_x), fake, fake, None, None, fake, fake, n, None) == moe.ERR_UNSUPPORTED
     d = moe.make_dims(64, 256, 16, 4, 64)
-    assert lib.moe_route_fused(ctypes.byref(d), None, fake, None, None, fake, None) == moe.ERR_NULL_ARG
-    assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, None, None) == moe.ERR_NULL_ARG
+    n = moe.moe_workspace_bytes(d)
+    assert lib.moe_route_fused(ctypes.byref(d), None, fake, None, None, fake, fake, n, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, None, fake, n, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, fake, None, n, None) == moe.ERR_NULL_ARG
+    assert lib.moe_route_fused(ctypes.byref(d), fake, fake, None, None, fake, fake, n - 1, None) == moe.ERR_WORKSPACE
     zero = moe.make_dims(0, 256, 16, 4, 64)
-    assert lib.moe_route_fused(ctypes.byref(zero), fake, fake, None, None, fake, None) == moe.OK
+    assert lib.moe_route_fused(ctypes.byref(zero), fake, fake, None, None, fake, fake, 1 << 20, None) == moe.OK
 
 
 def test_audit_argument_checks():
