@@ -455,7 +455,9 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   const void* a_rows = x;
   const float* a_scale = nullptr;
   if (fp8) {
-    MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s));
+    // tokens without a local slot (other devices' experts only) are not quantised
+    MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s, inv,
+                              d.top_k));
     a_rows = at<void>(ws, L.xq);
     a_scale = at<float>(ws, L.sx);
   }

@@ -119,8 +119,10 @@ hipError_t launch_gather_rows(const void* src, const float* src_scale, const int
                               const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,
                               hipStream_t stream);
 
+// Per-row E4M3 quantisation.  skip_inv (nullable): inv_pos [rows][skip_k]; rows whose slots are
+// all non-local are skipped (left unwritten: the grouped GEMMs never read them).
 hipError_t launch_quant_rows(int in_el, const void* src, int rows, const int32_t* n_rows_dev, int cols, void* dst,
-                             float* scale, hipStream_t stream);
+                             float* scale, hipStream_t stream, const int32_t* skip_inv = nullptr, int skip_k = 0);
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int n_groups, int bm0, int bm1, int32_t* prefix0,
                               int32_t* prefix1, hipStream_t stream);

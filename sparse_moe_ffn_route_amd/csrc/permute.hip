@@ -25,6 +25,7 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 
 constexpr int kUnitSteps = kPermUnit / kWave;  // 64-pair steps of one unit (16)
+constexpr int kScanLds = 16384;                // histogram entries the scan stages in LDS (64 KB)
 
 // Local expert of pair i of the token-major list, -1 if the expert is not local.
 __device__ __forceinline__ int local_expert(const int32_t* packed, int i, int k, int e_begin, int n_local) {
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ err_word) {
   __shared__ int32_t sc[3][1024];
   __shared__ int32_t sbad[1024 / kWave];
+  __shared__ int32_t sh[kScanLds];  // the whole histogram, when it fits
   const int e = threadIdx.x;
   {
     int nb = 0;
@@ -112,10 +114,19 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     nb = wave_sum_int(nb);
     if (lane_id() == 0) sbad[e / kWave] = nb;
   }
+  // A histogram that fits in LDS is loaded by the whole workgroup in one coalesced sweep
+  // (one memory latency), rather than unit by unit by each expert's thread.
+  const int n_hist = n_units * n_local;
+  const bool in_lds = n_hist <= kScanLds;
+  if (in_lds) {
+    for (int i = e; i < n_hist; i += 1024) sh[i] = hist[i];
+    __syncthreads();
+  }
+  const int32_t* hsrc = in_lds ? sh : hist;
   int tot = 0;
   if (e < n_local) {
 #pragma unroll 8
-    for (int u = 0; u < n_units; ++u) tot += hist[static_cast<size_t>(u) * n_local + e];
+    for (int u = 0; u < n_units; ++u) tot += hsrc[static_cast<size_t>(u) * n_local + e];
   }
   sc[0][e] = tot;
   sc[1][e] = (tot + bm0 - 1) / bm0;
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
 #pragma unroll 8
     for (int u = 0; u < n_units; ++u) {
       const size_t at = static_cast<size_t>(u) * n_local + e;
-      const int c = hist[at];
+      const int c = hsrc[at];
       base[at] = run;
       run += c;
     }
@@ -382,14 +393,21 @@ __device__ __forceinline__ void quant_row_in_regs(const void* __restrict__ src, 
   if (lane == 0) scale[r] = s;
 }
 
+// skip_inv: NULL, or inv_pos [rows][skip_k]: a row whose k slots are all non-local
+// (inv_pos < 0) is never read by the grouped GEMMs and is left unwritten.
 template <int IN>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int rows,
                                                          const int32_t* __restrict__ n_rows_dev, int cols,
-                                                         uint8_t* __restrict__ dst, float* __restrict__ scale) {
+                                                         uint8_t* __restrict__ dst, float* __restrict__ scale,
+                                                         const int32_t* __restrict__ skip_inv, int skip_k) {
   const int r = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int lane = lane_id();
   const int n = n_rows_dev ? *n_rows_dev : rows;
   if (r >= n) return;
+  if (skip_inv) {
+    const bool used = lane < skip_k && skip_inv[static_cast<size_t>(r) * skip_k + lane] >= 0;
+    if (__ballot(used) == 0) return;  // wave-uniform
+  }
   if (cols <= kWave * 8 * 2) return quant_row_in_regs<IN, 2>(src, r, cols, lane, dst, scale);
   if (cols <= kWave * 8 * 4) return quant_row_in_regs<IN, 4>(src, r, cols, lane, dst, scale);
   if (cols <= kWave * 8 * 8) return quant_row_in_regs<IN, 8>(src, r, cols, lane, dst, scale);
@@ -514,15 +532,15 @@ hipError_t launch_gather_rows(const void* src, const float* src_scale, const int
 }
 
 hipError_t launch_quant_rows(int in_el, const void* src, int rows, const int32_t* n_rows_dev, int cols, void* dst,
-                             float* scale, hipStream_t stream) {
+                             float* scale, hipStream_t stream, const int32_t* skip_inv, int skip_k) {
   if (rows == 0) return hipSuccess;
   dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
   if (in_el == EL_BF16)
     hipLaunchKernelGGL(quant_rows_kernel<EL_BF16>, grid, dim3(256), 0, stream, src, rows, n_rows_dev, cols,
-                       static_cast<uint8_t*>(dst), scale);
+                       static_cast<uint8_t*>(dst), scale, skip_inv, skip_k);
   else
     hipLaunchKernelGGL(quant_rows_kernel<EL_F32>, grid, dim3(256), 0, stream, src, rows, n_rows_dev, cols,
-                       static_cast<uint8_t*>(dst), scale);
+                       static_cast<uint8_t*>(dst), scale, skip_inv, skip_k);
   return hipGetLastError();
 }
 
