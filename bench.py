@@ -60,7 +60,7 @@ def kernel_source_hash():
     """Hash of the sources the grouped GEMM kernel is built from (its traffic figures are void once these change)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_ffn_route_amd", "csrc")
-    for f in ("common.hpp", "kernels.hpp", "gemm.hip"):
+    for f in ("common.hpp", "gemm.hpp", "gemm.hip"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -41,7 +41,7 @@
 #include <type_traits>
 
 #include "common.hpp"
-#include "kernels.hpp"
+#include "gemm.hpp"
 
 namespace moe {
 
