@@ -38,34 +38,43 @@ constexpr int kWRing = 3;                // weight blocks in the register ring (
 
 // KS: 64-byte K steps per block.  A wave streams the W_r rows of its NFW 16 experts, so its
 // bytes in flight are 2 blocks x NFW x KS KB: long blocks keep the stream from being
-// latency-bound.
-template <int EL, int TB, int NFW, int KS>
-__global__ __launch_bounds__(256) void router_slice_kernel(const void* __restrict__ x,
-                                                           const void* __restrict__ w_router,
-                                                           const float* __restrict__ bias, int T, int D, int E,
-                                                           int k, int n_slices, float* __restrict__ logits_out,
-                                                           float* __restrict__ cand_key, int32_t* __restrict__ cand_id,
-                                                           float2* __restrict__ stats) {
+// latency-bound.  KG: groups of 4 waves that split D into KG equal ranges (a workgroup of
+// 256 KG threads); their partial tiles are added in group order in LDS, so the logits
+// still have one fixed summation order.
+template <int EL, int TB, int NFW, int KS, int KG>
+__global__ __launch_bounds__(256 * KG) void router_slice_kernel(const void* __restrict__ x,
+                                                                const void* __restrict__ w_router,
+                                                                const float* __restrict__ bias, int T, int D, int E,
+                                                                int k, int n_slices, float* __restrict__ logits_out,
+                                                                float* __restrict__ cand_key,
+                                                                int32_t* __restrict__ cand_id,
+                                                                float2* __restrict__ stats) {
   constexpr int kKSteps = KS;
   constexpr int kKBlk = kKSteps * 64;     // bytes of each row per K block
   constexpr int kRow = kKBlk + 16;        // padded LDS row of the token tile (bytes)
   constexpr int SW = 4 * NFW * 16;        // experts per slice
   constexpr int MF = TB / 16;             // 16-token B fragments
   constexpr int LOG_ROW = SW + 4;         // padded LDS row of the logits tile (floats)
-  constexpr int TOK_BYTES = 2 * TB * kRow;
-  constexpr int LOG_BYTES = TB * LOG_ROW * 4;
+  constexpr int TOK_BYTES = KG * 2 * TB * kRow;
+  constexpr int LOG_BYTES = KG * TB * LOG_ROW * 4;
   constexpr int LDS_BYTES = TOK_BYTES > LOG_BYTES ? TOK_BYTES : LOG_BYTES;
   constexpr int ES = ElSize<EL>::v;
   constexpr int PL = SW / kWave;          // slice keys per lane
+  constexpr int NW = 4 * KG;              // waves of the workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int s = blockIdx.x % n_slices;
   const int t0 = (blockIdx.x / n_slices) * TB;
   const int e0 = s * SW;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int gw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave of the workgroup
+  const int kg = gw / 4, wv = gw % 4;                                 // K group, wave in the group
+  const int tid = threadIdx.x % 256;                                  // thread in the group
   const int lane = threadIdx.x % kWave, lrow = lane & 15, lgrp = lane >> 4;
   const uint32_t row_bytes = static_cast<uint32_t>(D) * ES;
-  const int nblk = static_cast<int>(row_bytes / kKBlk);  // the host keeps row_bytes a multiple of kKBlk
+  // the host keeps row_bytes a multiple of KG * kKBlk
+  const int nblk = static_cast<int>(row_bytes / kKBlk) / KG;  // K blocks of this group
+  const uint32_t kofs = static_cast<uint32_t>(kg * nblk) * kKBlk;
+  uint8_t* tok = lds + kg * 2 * TB * kRow;
 
   // operand offsets: W_r rows past E and token rows past T re-read the last valid row
   // (their results are never used)
@@ -80,14 +89,14 @@ __global__ __launch_bounds__(256) void router_slice_kernel(const void* __restric
   constexpr int kCpr = kKBlk / 16;                      // 16-byte chunks per token row per block
   constexpr int kChunks = TB * kCpr;                    // chunks of the token tile per block
   constexpr int kPasses = (kChunks + 255) / 256;
-  const int crow = threadIdx.x / kCpr, ccol = (threadIdx.x % kCpr) * 16;
+  const int crow = tid / kCpr, ccol = (tid % kCpr) * 16;
   uint32_t toff[kPasses];
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const int t = min(t0 + min(crow + i * (256 / kCpr), TB - 1), T - 1);
     toff[i] = static_cast<uint32_t>(t) * row_bytes + ccol;
   }
-  const bool loads_tokens = kChunks >= 256 || static_cast<int>(threadIdx.x) < kChunks;
+  const bool loads_tokens = kChunks >= 256 || tid < kChunks;
 
   f32x4 acc[NFW][MF];
 #pragma unroll
@@ -98,14 +107,14 @@ __global__ __launch_bounds__(256) void router_slice_kernel(const void* __restric
   u32x4 wr[kWRing][NFW][kKSteps];
   u32x4 tv[kPasses];
   auto ld_w = [&](u32x4 (&w)[NFW][kKSteps], int kb) {
-    const uint32_t o = static_cast<uint32_t>(min(kb, nblk - 1)) * kKBlk;
+    const uint32_t o = kofs + static_cast<uint32_t>(min(kb, nblk - 1)) * kKBlk;
 #pragma unroll
     for (int st = 0; st < kKSteps; ++st)
 #pragma unroll
       for (int nf = 0; nf < NFW; ++nf) w[nf][st] = buffer_load16(wres, woff[nf], o + st * 64);
   };
   auto ld_t = [&](int kb) {
-    const uint32_t o = static_cast<uint32_t>(min(kb, nblk - 1)) * kKBlk;
+    const uint32_t o = kofs + static_cast<uint32_t>(min(kb, nblk - 1)) * kKBlk;
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) tv[i] = buffer_load16(xres, toff[i], o);
   };
@@ -113,10 +122,10 @@ __global__ __launch_bounds__(256) void router_slice_kernel(const void* __restric
     if (!loads_tokens) return;
 #pragma unroll
     for (int i = 0; i < kPasses; ++i)
-      *reinterpret_cast<u32x4*>(&lds[buf * TB * kRow + (crow + i * (256 / kCpr)) * kRow + ccol]) = tv[i];
+      *reinterpret_cast<u32x4*>(&tok[buf * TB * kRow + (crow + i * (256 / kCpr)) * kRow + ccol]) = tv[i];
   };
   auto mm = [&](const u32x4 (&w)[NFW][kKSteps], int buf) {
-    const uint8_t* sb = &lds[buf * TB * kRow + lrow * kRow + lgrp * 16];
+    const uint8_t* sb = &tok[buf * TB * kRow + lrow * kRow + lgrp * 16];
 #pragma unroll
     for (int st = 0; st < kKSteps; ++st)
 #pragma unroll
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(256) void router_slice_kernel(const void* __restric
   };
 
   // K blocks: weights two blocks ahead in a three-block register ring, token rows one
-  // block ahead through registers into the other LDS buffer
+  // block ahead through registers into the other LDS buffer of the group
   ld_t(0);
   ld_w(wr[0], 0);
   ld_w(wr[1], 1);
@@ -146,19 +155,31 @@ __global__ __launch_bounds__(256) void router_slice_kernel(const void* __restric
     }
   }
 
-  // logits tile to LDS: lane holds experts 4 (l / 16) + r of each fragment for token l % 16
+  // partial logits tiles to LDS (group kg's at kg * TB rows): lane holds experts
+  // 4 (l / 16) + r of each fragment for token l % 16; then the groups' partials are added
+  // in group order into group 0's tile
   float* lt = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int nf = 0; nf < NFW; ++nf)
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
       const int c = wv * NFW * 16 + nf * 16 + lgrp * 4;
-      *reinterpret_cast<f32x4*>(&lt[(mf * 16 + lrow) * LOG_ROW + c]) = acc[nf][mf];
+      *reinterpret_cast<f32x4*>(&lt[(kg * TB + mf * 16 + lrow) * LOG_ROW + c]) = acc[nf][mf];
     }
   __syncthreads();
+  if constexpr (KG > 1) {
+    for (int i = threadIdx.x; i < TB * SW; i += 256 * KG) {
+      const int r = i / SW, c = i % SW;
+      float v = lt[r * LOG_ROW + c];
+#pragma unroll
+      for (int g = 1; g < KG; ++g) v += lt[(g * TB + r) * LOG_ROW + c];
+      lt[r * LOG_ROW + c] = v;
+    }
+    __syncthreads();
+  }
 
   // each wave: top-k of the slice for its tokens
-  for (int r = wv; r < TB; r += 4) {
+  for (int r = gw; r < TB; r += NW) {
     const int t = t0 + r;
     if (t >= T) break;
     float key[PL];
@@ -305,17 +326,25 @@ hipError_t launch_slices(const void* x, const void* w_router, const float* bias,
   constexpr int SW = 4 * NFW * 16;
   const int n_slices = (E + SW - 1) / SW;
   const dim3 grid(n_slices * ((T + TB - 1) / TB));
-  // the longest K block (512, 256 or 128 bytes) that divides the row
+  // small batches split D over 4 wave groups (16 waves per workgroup) when the row holds
+  // 4 x 256 bytes; otherwise the longest K block (512, 256 or 128 bytes) that divides the row
   const int row_bytes = D * ElSize<EL>::v;
+  if constexpr (TB == 16) {
+    if (row_bytes % 1024 == 0) {
+      hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 4, 4>), grid, dim3(1024), 0, stream, x, w_router, bias,
+                         T, D, E, k, n_slices, logits_out, cand_key, cand_id, stats);
+      return hipGetLastError();
+    }
+  }
   if (row_bytes % 512 == 0)
-    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 8 / NFW>), grid, dim3(256), 0, stream, x, w_router, bias,
-                       T, D, E, k, n_slices, logits_out, cand_key, cand_id, stats);
+    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 8 / NFW, 1>), grid, dim3(256), 0, stream, x, w_router,
+                       bias, T, D, E, k, n_slices, logits_out, cand_key, cand_id, stats);
   else if (row_bytes % 256 == 0)
-    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 4>), grid, dim3(256), 0, stream, x, w_router, bias, T, D,
-                       E, k, n_slices, logits_out, cand_key, cand_id, stats);
+    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 4, 1>), grid, dim3(256), 0, stream, x, w_router, bias, T,
+                       D, E, k, n_slices, logits_out, cand_key, cand_id, stats);
   else
-    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 2>), grid, dim3(256), 0, stream, x, w_router, bias, T, D,
-                       E, k, n_slices, logits_out, cand_key, cand_id, stats);
+    hipLaunchKernelGGL((router_slice_kernel<EL, TB, NFW, 2, 1>), grid, dim3(256), 0, stream, x, w_router, bias, T,
+                       D, E, k, n_slices, logits_out, cand_key, cand_id, stats);
   return hipGetLastError();
 }
 
