@@ -70,7 +70,21 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
 // rate at the clock the chip holds under that load.  bf16: 16x16x32 (16384 FLOP per
 // MFMA); E4M3: 16x16x128 of the f8f6f4 family (65536 FLOP).  Lane 0 of each workgroup
 // writes the sum of its accumulators to sink, so the work cannot be dropped.
+//
+// Each chain has its own B operand and the first round is peeled, so the loop carries
+// eight distinct MFMA results.  With identical chains started from zero accumulators the
+// compiler merges them and then rotates the 16x16 bf16 accumulators through AGPR copies
+// every round (about 50 moves per 8 MFMAs), which caps the loop at about 55% of the
+// matrix cores' rate; in this form the loop is 8 MFMAs and the branch.
 constexpr int kProbeChains = 8;
+
+template <int EL>
+__device__ __forceinline__ f32x4 probe_mfma(const u32x4& a, const u32x4& b, f32x4 c) {
+  if constexpr (EL == EL_E4M3)
+    return mfma_e4m3_pair(a, b, b, a, c);
+  else
+    return mfma_chunk<EL_BF16>(a, b, c);
+}
 
 template <int EL>
 __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
@@ -78,23 +92,21 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
   const uint32_t base = EL == EL_E4M3 ? 0x38383838u : 0x3C003C00u;
   const uint32_t t = threadIdx.x & 3;
   const u32x4 a = {base, base ^ (t << 8), base, base ^ t};
-  const u32x4 b = {base ^ t, base, base ^ (t << 8), base};
+  u32x4 b[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c) b[c] = u32x4{base ^ t, base ^ (uint32_t)c, base ^ (t << 8), base};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[kProbeChains];
 #pragma unroll
-  for (int c = 0; c < kProbeChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < iters; ++i) {
+  for (int c = 0; c < kProbeChains; ++c) acc[c] = probe_mfma<EL>(a, b[c], zero);
+  for (int i = 1; i < iters; ++i) {
 #pragma unroll
-    for (int c = 0; c < kProbeChains; ++c) {
-      if constexpr (EL == EL_E4M3)
-        acc[c] = mfma_e4m3_pair(a, b, b, a, acc[c]);
-      else
-        acc[c] = mfma_chunk<EL_BF16>(a, b, acc[c]);
-    }
+    for (int c = 0; c < kProbeChains; ++c) acc[c] = probe_mfma<EL>(a, b[c], acc[c]);
   }
-  float s = 0.f;
+  f32x4 s = acc[0];
 #pragma unroll
-  for (int c = 0; c < kProbeChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
-  if (threadIdx.x == 0) sink[blockIdx.x] = s;
+  for (int c = 1; c < kProbeChains; ++c) s += acc[c];
+  if (threadIdx.x == 0) sink[blockIdx.x] = s[0] + s[1] + s[2] + s[3];
 }
 
 }  // namespace
