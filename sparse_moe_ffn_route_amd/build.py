@@ -84,7 +84,9 @@ def build(verbose: bool = False, extra_flags=(), incremental: bool = False) -> s
             if msg and verbose:
                 print(msg, file=sys.stderr)
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: a symbol left undefined (e.g. a kernel whose host stub was not emitted)
+    # fails the link here instead of the library's load
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")

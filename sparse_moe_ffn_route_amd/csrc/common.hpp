@@ -59,6 +59,31 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
 }
 
+// Direct buffer-to-LDS load: every lane reads 16 bytes at the resource's base + voff +
+// soff and they land in LDS at lds_wave_base + 16 * lane (one contiguous 1 KB per wave;
+// lds_wave_base must be wave-uniform).  Counted by vmcnt like any vector load.
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
+                                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                           0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding (N <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence (the compiler's fence would wait for every
+// vector load in flight while LDS-bound loads are outstanding); memory operations are
+// kept on their side of it.  Callers make their own LDS writes complete first.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Two floats -> two bfloat16 (low half = a), round to nearest even; one gfx950 convert.
 __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
