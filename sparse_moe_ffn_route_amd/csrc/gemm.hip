@@ -802,13 +802,10 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
 // 128-byte line is split over two load instructions, and the hint costs bandwidth.
 // stream16 with 16-bit weights: one workgroup per CU and a four-block weight ring
 // (three blocks in flight per wave) keeps more bytes in flight than two workgroups with
-// a two-block ring; with E4M3 weights two workgroups per CU measured faster.  The packed
-// bf16 gate/up takes two fragments per matrix per wave in 4-step blocks (same registers
-// and bytes in flight as one fragment in 8-step blocks): half as many workgroups, each
-// streaming 2 MB, which measured 2 % faster than 1 MB workgroups.
+// a two-block ring; with E4M3 weights two workgroups per CU measured faster.
 template <int EL, int SHAPE, bool SWIGLU, bool PACKED> struct Shape;
 template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream16, SWIGLU, PACKED> {
-  static constexpr int MF = 1, KSTEPS = SWIGLU ? (EL == EL_BF16 && PACKED ? 4 : 8) : 4, TDEPTH = 1;
+  static constexpr int MF = 1, KSTEPS = SWIGLU ? 8 : 4, TDEPTH = 1;
   static constexpr int NBUF = EL == EL_E4M3 ? 2 : 4, MINB = EL == EL_E4M3 ? 2 : 1;
   static constexpr bool NT = PACKED;
 };

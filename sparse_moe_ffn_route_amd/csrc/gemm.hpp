@@ -54,7 +54,7 @@ constexpr int gemm_bm(int shape) { return shape == kShapeStream16 ? 16 : shape =
 // packed: fragment-major weights.  Host tile counts and kernels both take it from here.
 constexpr int gemm_nf(bool swiglu, int shape, int el, bool packed) {
   return shape == kShapeTile256 ? (swiglu || el == EL_E4M3 || packed ? 2 : 4)
-                                : shape == kShapeStream16 ? (swiglu ? (el == EL_BF16 && packed ? 2 : 1) : 4) : (swiglu ? 1 : 2);
+                                : shape == kShapeStream16 ? (swiglu ? 1 : 4) : (swiglu ? 1 : 2);
 }
 // Output channels per workgroup (4 waves).
 constexpr int gemm_bn(bool swiglu, int shape, int el, bool packed) {

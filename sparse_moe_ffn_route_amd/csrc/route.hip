@@ -14,10 +14,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kMaxPerLane = kMaxKeysPerLane;
-
 // SPLIT: the router product arrives as n_parts > 1 partial sums over slices of D.
-template <bool SPLIT>
+// kMaxPerLane: keys per lane (E <= 64 * kMaxPerLane).
+template <bool SPLIT, int kMaxPerLane>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ parts, int n_parts,
                                                     float* __restrict__ logits, const float* __restrict__ bias,
                                                     int T, int E, int k, int renormalize,
@@ -75,12 +74,23 @@ hipError_t launch_route(const float* parts, int n_parts, float* logits, const fl
   if (T == 0) return hipSuccess;
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  if (n_parts > 1)
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits,
-                       bias, T, E, k, renormalize, packed);
-  else
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(waves_per_block * kWave), 0, stream, parts, n_parts, logits,
-                       bias, T, E, k, renormalize, packed);
+  const dim3 block(waves_per_block * kWave);
+  // keys per lane: 8 cover up to 512 experts, kMaxKeysPerLane the largest E accepted
+  if (E <= 8 * kWave) {
+    if (n_parts > 1)
+      hipLaunchKernelGGL((route_kernel<true, 8>), grid, block, 0, stream, parts, n_parts, logits, bias, T, E, k,
+                         renormalize, packed);
+    else
+      hipLaunchKernelGGL((route_kernel<false, 8>), grid, block, 0, stream, parts, n_parts, logits, bias, T, E, k,
+                         renormalize, packed);
+  } else {
+    if (n_parts > 1)
+      hipLaunchKernelGGL((route_kernel<true, kMaxKeysPerLane>), grid, block, 0, stream, parts, n_parts, logits, bias,
+                         T, E, k, renormalize, packed);
+    else
+      hipLaunchKernelGGL((route_kernel<false, kMaxKeysPerLane>), grid, block, 0, stream, parts, n_parts, logits, bias,
+                         T, E, k, renormalize, packed);
+  }
   return hipGetLastError();
 }
 

@@ -24,6 +24,44 @@ __device__ __forceinline__ bool key_before(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// (bk, bi) <- the better of itself and the pair held by the lane that DPP control CTRL
+// selects (a VALU operand modifier: no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ void dpp_best(float& bk, int& bi) {
+  const float ok = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bk), __float_as_int(bk), CTRL, 0xF, 0xF,
+                                                              false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, 0xF, 0xF, false);
+  if (key_before(ok, oi, bk, bi)) {
+    bk = ok;
+    bi = oi;
+  }
+}
+
+// Wave-wide best (key, index) pair, returned to every lane.  Within each 16-lane row:
+// quad exchanges (lane ^ 1, lane ^ 2), then the half-row mirror (lane i <-> 7 - i of each
+// 8) and the row mirror (i <-> 15 - i), after which every lane of a row holds the row's
+// best; the four row winners are then read out and compared.  The order is a strict
+// total order on (key, index), so the result does not depend on the reduction's shape.
+__device__ __forceinline__ void wave_best(float& bk, int& bi) {
+  dpp_best<0xB1>(bk, bi);   // quad_perm [1, 0, 3, 2]
+  dpp_best<0x4E>(bk, bi);   // quad_perm [2, 3, 0, 1]
+  dpp_best<0x141>(bk, bi);  // row_half_mirror
+  dpp_best<0x140>(bk, bi);  // row_mirror
+  float rk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bk), 0));
+  int ri = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ok = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bk), 16 * r));
+    const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
+    if (key_before(ok, oi, rk, ri)) {
+      rk = ok;
+      ri = oi;
+    }
+  }
+  bk = rk;
+  bi = ri;
+}
+
 // key[i] for i < PL: keys as above; entries of experts >= E are ignored.  Writes the
 // token's ids to out[0..k) and the weights' bits to out[k..2k).
 template <int PL>
@@ -49,16 +87,7 @@ __device__ __forceinline__ void select_topk(const float (&key)[PL], int E, int k
         bi = e;
       }
     }
-    // wave-wide arg-best
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (key_before(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-      }
-    }
+    wave_best(bk, bi);
     if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == j) {
       sel_key = bk;
