@@ -817,7 +817,8 @@ template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeStream32, SWI
 // projection keeps its row-major shape): K is short (I = 1024), so a tile runs few K
 // blocks and its prologue and epilogue weigh; 2 fragments per wave, a two-block ring
 // and one block of token lookahead fit two workgroups per CU, which overlap one
-// another's ends (the compiler spills ~32 VGPRs there; measured faster nonetheless).
+// another's ends (for e4m3 the compiler keeps four 64-bit values in scratch outside the
+// K loop; one workgroup per CU with 4 fragments per wave measured slower for both).
 template <int EL, bool SWIGLU, bool PACKED> struct Shape<EL, kShapeTile256, SWIGLU, PACKED> {
   static constexpr bool kTwoPerCu = !SWIGLU && (EL == EL_E4M3 || PACKED);
   static constexpr int MF = 16, KSTEPS = 2, NBUF = kTwoPerCu ? 2 : 4, MINB = kTwoPerCu ? 2 : 1;
