@@ -56,12 +56,38 @@ def parse():
     return p.parse_args()
 
 
+def code_tokens(text):
+    """C++ source without comments and with each run of whitespace as one space (string and character
+    literals kept as they are), so that editing a comment leaves the result unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """Hash of the sources the grouped GEMM kernel is built from (its traffic figures are void once these change)."""
+    """Hash of the code the grouped GEMM kernel is built from, comments excluded (its traffic figures are void
+    once the code changes)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_ffn_route_amd", "csrc")
     for f in ("common.hpp", "gemm.hpp", "gemm.hip"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(code_tokens(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
