@@ -6,10 +6,10 @@
 // Mixture-of-Experts (MoE)" in "Tối ưu hóa mô hình Qwen 3.5-397B MoE trên hạ tầng TPU
 // Ironwood", whose formula is missing.
 //
-// Work unit (one 256-thread workgroup): one (group, N-tile, M-tile).  The M-tile is up
-// to 16 * MF token rows of the group (gathered through perm); the N-tile is
-// 4 waves x NF x 16 output channels (for SwiGLU the same channels of W_gate and W_up,
-// so silu(gate) * up is formed in registers).
+// Work unit (one workgroup of NW waves: 4, or 8 for the router projection's tiles): one
+// (group, N-tile, M-tile).  The M-tile is up to 16 * MF token rows of the group (gathered
+// through perm); the N-tile is NW waves x NF x 16 output channels (for SwiGLU the same
+// channels of W_gate and W_up, so silu(gate) * up is formed in registers).
 //
 // Data path:
 //   * weights go straight from HBM into VGPRs as the MFMA "A" operand; each wave owns
@@ -96,17 +96,18 @@ struct TileInfo {
 // COMB: the epilogue is the fused unpermute-combine of a single-group problem (see
 // GemmProblem::comb_rows), instantiated for the shared expert's down projection only.
 template <int EL, int OUT, int MF, int NF, bool SWIGLU, int KSTEPS, int NBUF, bool NTW, int MINB, bool PACKED,
-          int TDEPTH, bool COMB>
-__global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
+          int TDEPTH, bool COMB, int NW>
+__global__ __launch_bounds__(NW * 64, MINB) void gemm_kernel(GemmProblem p) {
   constexpr int ES = ElSize<EL>::v;
   constexpr int BM = 16 * MF;
   constexpr int NMAT = SWIGLU ? 2 : 1;
-  constexpr int BN = 4 * NF * 16;
+  constexpr int NTHR = NW * kWave;    // threads per workgroup
+  constexpr int BN = NW * NF * 16;
   constexpr int KBLK = KSTEPS * 64;   // bytes of each row per K block
   constexpr int LDS_ROW = KBLK + 16;  // padded LDS row (bytes)
   constexpr int CHUNKS = BM * (KBLK / 16);
-  static_assert(CHUNKS % 256 == 0, "token tile must split evenly over 256 threads");
-  constexpr int CPT = CHUNKS / 256;   // 16-byte token chunks per thread per K block
+  static_assert(CHUNKS % NTHR == 0, "token tile must split evenly over the threads");
+  constexpr int CPT = CHUNKS / NTHR;  // 16-byte token chunks per thread per K block
   // LDS token staging.  Streaming shapes: two buffers of padded rows (LDS_ROW bytes)
   // written from registers.  Tile shape: TDEPTH + 1 buffers of unpadded KBLK-byte rows in
   // a swizzled chunk order, filled by direct buffer-to-LDS loads.
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
       constexpr int PR = PR2 >= 64 && BM % 64 == 0 ? 64 : PR2 >= 32 && BM % 32 == 0 ? 32 : 16;  // rows per pass
       static_assert(PR * ROW_BYTES <= LDS_BYTES && BM % PR == 0, "combine staging pass must fit the LDS");
       constexpr int TPR = BN / 8;                           // threads per row (8 columns each)
-      constexpr int RPI = 256 / TPR;                        // rows per workgroup sweep
+      constexpr int RPI = NTHR / TPR;                       // rows per workgroup sweep
       constexpr int R = PR / RPI;                           // rows per thread per pass
       static_assert(R >= 1 && PR % RPI == 0, "rows per pass must split evenly over the threads");
       constexpr int PIECES = OUT == EL_F32 ? 2 : 1;         // 16-byte loads per 8-column piece
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
         // contiguous run of inv, their weights plane 1 of each token's blob
         const int rows = min(PR, t.nrows - pass * PR);
         const int tok0 = t.row0 + t.rbeg + pass * PR;
-        for (int q = threadIdx.x; q < rows * k; q += 256) {
+        for (int q = threadIdx.x; q < rows * k; q += NTHR) {
           const int r = q / k, j = q - r * k;
           s_inv[r * KMAX + j] = p.comb_inv[static_cast<size_t>(tok0) * k + q];
           s_w[r * KMAX + j] = __int_as_float(p.comb_packed[(static_cast<size_t>(tok0) + r) * 2 * k + k + j]);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
     }
     constexpr int CPR = KBLK / 16;        // 16-byte chunks per token row per K block
     static_assert(CPR == 8, "tile shape: 128-byte K blocks");
-    constexpr int RPP = 256 / CPR;        // token rows per pass of the workgroup (4 KB)
+    constexpr int RPP = NTHR / CPR;       // token rows per pass of the workgroup (NW KB)
     constexpr int NTP = BM / RPP;         // passes for a full tile
     // Token rows go from memory straight into LDS (buffer loads with the LDS as
     // destination: no registers, no LDS store instructions).  An LDS row is the K block's
@@ -607,6 +608,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
     const int nfull = ti.nfull, tail_steps = ti.tail_steps;
     const int mf_active = (ti.nrows + 15) / 16;
     static_assert(NBUF >= 2 && NBUF <= 4, "streaming ring of 2 to 4 blocks");
+    static_assert(NW == 4, "streaming shapes: 4 waves");
 
     // Weights as buffer loads: a resource per matrix at the group's weights, a fixed
     // 32-bit offset per lane and fragment, and a wave-uniform offset per fragment to which
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_kernel(GemmProblem p) {
     int acol[CPT], aoff[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * 256;
+      const int c = threadIdx.x + i * NTHR;
       const int r = c / (KBLK / 16);
       acol[i] = (c % (KBLK / 16)) * 16;
       aoff[i] = r * LDS_ROW + acol[i];
@@ -830,10 +832,11 @@ template <int EL, int OUT, bool SWIGLU, int SHAPE, bool PACKED, bool COMB = fals
 hipError_t launch_one(const GemmProblem& p, int max_tiles, hipStream_t stream) {
   using S = Shape<EL, SHAPE, SWIGLU, PACKED>;
   constexpr int NF = gemm_nf(SWIGLU, SHAPE, EL, PACKED);
+  constexpr int NW = gemm_nw(SWIGLU, SHAPE, EL, PACKED);
   if (max_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(
-      (gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH, COMB>),
-      dim3(max_tiles), dim3(256), 0, stream, p);
+      (gemm_kernel<EL, OUT, S::MF, NF, SWIGLU, S::KSTEPS, S::NBUF, S::NT, S::MINB, PACKED, S::TDEPTH, COMB, NW>),
+      dim3(max_tiles), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -50,15 +50,20 @@ struct GemmProblem {
 enum : int { kShapeStream16 = 0, kShapeStream32 = 1, kShapeTile256 = 2 };
 
 constexpr int gemm_bm(int shape) { return shape == kShapeStream16 ? 16 : shape == kShapeStream32 ? 32 : 256; }
-// 16-column output fragments per wave (per matrix for SwiGLU).  el: weight element type;
-// packed: fragment-major weights.  Host tile counts and kernels both take it from here.
-constexpr int gemm_nf(bool swiglu, int shape, int el, bool packed) {
-  return shape == kShapeTile256 ? (swiglu || el == EL_E4M3 || packed ? 2 : 4)
-                                : shape == kShapeStream16 ? (swiglu ? 1 : 4) : (swiglu ? 1 : 2);
+// Waves per workgroup: the tile shape's single-matrix launches with row-major weights (the
+// router projection) run 8, two per SIMD; every other launch runs 4.  el: weight element
+// type; packed: fragment-major weights.
+constexpr int gemm_nw(bool swiglu, int shape, int el, bool packed) {
+  return shape == kShapeTile256 && !swiglu && !(el == EL_E4M3 || packed) ? 8 : 4;
 }
-// Output channels per workgroup (4 waves).
+// 16-column output fragments per wave (per matrix for SwiGLU).  Host tile counts and
+// kernels both take it from here.
+constexpr int gemm_nf(bool swiglu, int shape, int el, bool packed) {
+  return shape == kShapeTile256 ? 2 : shape == kShapeStream16 ? (swiglu ? 1 : 4) : (swiglu ? 1 : 2);
+}
+// Output channels per workgroup.
 constexpr int gemm_bn(bool swiglu, int shape, int el, bool packed) {
-  return 4 * gemm_nf(swiglu, shape, el, packed) * 16;
+  return gemm_nw(swiglu, shape, el, packed) * gemm_nf(swiglu, shape, el, packed) * 16;
 }
 
 // Grouped GEMM of one problem.
