@@ -51,8 +51,6 @@ int check_dims(const moe_dims* d) {
   return MOE_OK;
 }
 
-// Shape of the router projection: 32-row streaming tiles (E / 128 N-tiles per 32 tokens
-// already fill the chip at prefill sizes; small T is split along D instead).
 // Router projection shape: 256-row tiles once there are enough tokens for each W_r byte
 // to feed 256 of them (and x fits the tile shape's 32-bit offsets); 32-row streaming
 // tiles below that.

@@ -21,7 +21,7 @@
 //     buffer loads (a wave-uniform resource and offset plus one fixed offset per lane),
 //     so the loop computes no per-lane addresses and no load waits on a register that
 //     the compiler took from a pending load;
-//   * token rows are the MFMA "B" operand, shared by the 4 waves: staged per K block in
+//   * token rows are the MFMA "B" operand, shared by the workgroup's waves: staged per K block in
 //     LDS, one barrier per block.  The streaming shapes load them into registers and
 //     store them to two LDS buffers; the tile shape loads them straight into TDEPTH + 1
 //     LDS buffers, TDEPTH blocks ahead (no registers, no LDS store instructions).  Token
