@@ -213,6 +213,38 @@ def test_layer_forward_two_calls_reuse_workspace():
     np.testing.assert_array_equal(a["packed"], b["packed"])
 
 
+@pytest.mark.parametrize("name", ["decode_like_bf16", "fp8_shared_tile"])
+def test_layer_forward_runs_on_the_given_stream(name):
+    """Every launch of the layer goes to the stream it is given: on a second stream (default priority, ordered
+    after the inputs by an explicit wait), passed by the current-stream context and as an argument, y and the
+    routing blob equal the default-stream call's bit for bit."""
+    wl = MID[name]
+    ref = gpu_layer(synth.make_inputs(wl, 5, "cpu"))
+    dev = ref["dev"]
+    d = dims_of(wl)
+    w = moe.make_weights(dev.w_router, dev.w_gate, dev.w_up, dev.w_down, dev.s_gate, dev.s_up, dev.s_down,
+                         dev.ws_gate, dev.ws_up, dev.ws_down)
+    side = torch.cuda.Stream()
+    outs = []
+    for by_context in (True, False):
+        ws = moe.workspace(d)
+        y = torch.full((wl.T, wl.D), float("nan"), dtype=harness._OUT_TORCH[wl.out], device="cuda")
+        logits = None if wl.routing_given else torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
+        blob = torch.full((wl.T, 2, wl.top_k), -7, dtype=torch.int32, device="cuda")
+        side.wait_stream(torch.cuda.current_stream())
+        if by_context:
+            with torch.cuda.stream(side):
+                moe.moe_layer_forward(d, w, dev.x, dev.packed, dev.bias, y, logits, blob, ws)
+        else:
+            moe.moe_layer_forward(d, w, dev.x, dev.packed, dev.bias, y, logits, blob, ws, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        outs.append((harness.to_np(y), blob.cpu().numpy()))
+    for y, blob in outs:
+        np.testing.assert_array_equal(y, ref["y"])
+        np.testing.assert_array_equal(blob, ref["packed"])
+
+
 def test_stage_events_time_the_same_layer():
     """Stage events only mark the stream: y is bit-identical, and the marks are in stage order."""
     wl = MID["decode_like_bf16"]
