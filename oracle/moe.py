@@ -34,7 +34,7 @@ breaks off after its colon):
 
 import numpy as np
 
-from .numerics import f32_round, e4m3_round
+from .numerics import bf16_round, f32_round, e4m3_round
 
 
 # ---------------------------------------------------------------------------
@@ -280,7 +280,8 @@ def quantize_rows_e4m3(a):
     return e4m3_round(scaled.astype(np.float64)), s
 
 
-def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_begin=0, n_local=None):
+def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_begin=0, n_local=None,
+                           h_storage="bf16"):
     """The routed layer with e4m3 expert weights and per-output-channel scales.
 
     ``experts_q[e]`` returns ((g_q, g_s), (u_q, u_s), (d_q, d_s)): codes as
@@ -291,7 +292,11 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_be
     2. permute as in :func:`permute`;
     3. per expert: g = (x_q W_gq^T) s_x s_g, u likewise, h = silu(g) * u
        in float64;
-    4. quantise h per grouped row; out = (h_q W_dq^T) s_h s_d;
+    4. store h in the activation type (bfloat16: ``h_storage="bf16"``) and
+       quantise the stored rows per grouped row, so that h's codes are
+       decided from the values the layer keeps, as x's are from the given
+       bf16 x; out = (h_q W_dq^T) s_h s_d.  ``h_storage=None`` quantises
+       the float64 h itself (what the pin of each scale's place uses);
     5. combine with the routing weights, plus the shared expert when
        ``shared`` = (w_gate, w_up, w_down) is given.  The pages give the
        routed experts' fp8 storage only; the shared expert keeps the
@@ -300,6 +305,8 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_be
        partial sums go to a reduce-scatter and the shared expert is added
        once per token by the device that owns the token.
     """
+    if h_storage not in ("bf16", None):
+        raise ValueError(f"h_storage must be 'bf16' or None, not {h_storage!r}")
     x = np.asarray(x, dtype=np.float64)
     if n_local is None:
         n_local = len(experts_q)
@@ -307,7 +314,7 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_be
     counts, offsets, perm_token, inv_pos = permute(ids, expert_begin, n_local)
     D = x.shape[1]
     out = np.zeros((int(offsets[-1]), D), dtype=np.float64)
-    h_rows = [None] * n_local
+    h_rows = None
     for e in range(n_local):
         s, t = int(offsets[e]), int(offsets[e + 1])
         if s == t:
@@ -318,11 +325,15 @@ def layer_from_routing_fp8(x, ids, weights, experts_q, *, shared=None, expert_be
         g = (xq[rows] @ np.asarray(gq, np.float64).T) * xs * np.asarray(gs, np.float64)[None, :]
         u = (xq[rows] @ np.asarray(uq, np.float64).T) * xs * np.asarray(us, np.float64)[None, :]
         h = silu(g) * u
+        if h_storage == "bf16":
+            h = bf16_round(h)
+        if h_rows is None:
+            h_rows = np.zeros((int(offsets[-1]), h.shape[1]), dtype=np.float64)
+        h_rows[s:t] = h
         hq, hs = quantize_rows_e4m3(h)
         out[s:t] = (hq @ np.asarray(dq, np.float64).T) * hs.astype(np.float64)[:, None] \
             * np.asarray(ds, np.float64)[None, :]
-        h_rows[e] = h
     shared_out = swiglu_expert(x, *shared) if shared is not None else None
     y = combine(out, weights, inv_pos, shared_out)
     return dict(counts=counts, offsets=offsets, perm_token=perm_token, inv_pos=inv_pos,
-                x_q=xq, x_scale=sx, out_rows=out, shared_out=shared_out, y=y)
+                x_q=xq, x_scale=sx, h=h_rows, out_rows=out, shared_out=shared_out, y=y)

@@ -79,6 +79,19 @@ MID = {
     # fp8 expert-parallel slice at the same width with given routing (64-expert-share analogue)
     "tile_wide_fp8_slice": W("tile_wide_fp8_slice", T=4096, D=1024, E=64, top_k=8, I=512, I_shared=0,
                              act="bf16", w="e4m3", out="bf16", expert_begin=16, n_local=16, routing_given=True),
+    # ragged widths past one 512-column piece: D = 704 = 512 + 192, I = 320, I_s = 192.  Every expert GEMM ends
+    # on a partial N-tile (the 16-row streaming down projection's 256-channel tiles, the 256-row tiles'
+    # 128-channel ones, the fused combine's last tile); the streaming K loops end on a partial block (1408 and
+    # 640 bytes per row), the e4m3 tile gate/up on a lone 64-byte slice (704 bytes); a combine wave's second
+    # piece is partly past D
+    "ragged_decode_bf16": W("ragged_decode_bf16", T=128, D=704, E=32, top_k=4, I=320, I_shared=192, act="bf16",
+                            w="bf16", out="bf16"),
+    "ragged_tile_bf16": W("ragged_tile_bf16", T=2048, D=704, E=16, top_k=2, I=320, I_shared=192, act="bf16",
+                          w="bf16", out="bf16"),
+    "ragged_tile_fp8": W("ragged_tile_fp8", T=2048, D=704, E=16, top_k=2, I=320, I_shared=192, act="bf16",
+                         w="e4m3", out="bf16"),
+    "ragged_slice_fp8": W("ragged_slice_fp8", T=1024, D=704, E=16, top_k=4, I=320, I_shared=0, act="bf16",
+                          w="e4m3", out="bf16", expert_begin=4, n_local=8, routing_given=True),
 }
 
 
@@ -108,7 +121,8 @@ def test_layer_forward_parity(name):
 @pytest.mark.parametrize("name", ["tiny_fp32", "mid_fp32", "decode_like_bf16", "mid_bf16", "mid_bf16_f32out",
                                   "skew_bf16", "slice_fp8", "slice_fp8_f32out", "fp8_shared", "fp8_shared_tile",
                                   "one_token", "tile_bf16_f32out", "tile_wide_bf16", "tile_wide_fp8",
-                                  "tile_wide_skew_bf16", "tile_wide_fp8_slice"])
+                                  "tile_wide_skew_bf16", "tile_wide_fp8_slice", "ragged_decode_bf16",
+                                  "ragged_tile_bf16", "ragged_tile_fp8", "ragged_slice_fp8"])
 def test_layer_forward_parity_packed_weights(name):
     """Expert weights repacked by moe_pack_weights (fragment-major layout) give the same layer."""
     _check_layer(MID[name], seed=2, packed=True)
@@ -197,7 +211,8 @@ def test_pack_weights_layout():
 
 
 @pytest.mark.parametrize("name", ["mid_bf16", "decode_like_bf16", "tiny_fp32", "skew_bf16", "tile_wide_bf16",
-                                  "tile_wide_fp8", "fp8_shared_tile"])
+                                  "tile_wide_fp8", "fp8_shared_tile", "ragged_decode_bf16", "ragged_tile_bf16",
+                                  "ragged_tile_fp8"])
 def test_layer_forward_parity_without_shared_expert(name):
     """The shared expert dominates y; without it a routed-path error cannot hide under the tolerance."""
     _check_layer(MID[name], seed=1, shared=False)

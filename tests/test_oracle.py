@@ -436,8 +436,9 @@ def _fp8_weights(rng, n, out_dim, in_dim):
 
 def test_fp8_share_with_single_intermediate_channel_is_exact_layer_on_dequantised_inputs():
     """With I = 1 each h row has one value, which the per-row quantiser maps to +-448 * s_h
-    (exact up to fp32 rounding of the scale), so the fp8 share must equal the exact layer
-    evaluated on the dequantised x and weights: this pins where every scale enters."""
+    (exact up to fp32 rounding of the scale), so the fp8 share, quantising its float64 h
+    (h_storage=None), must equal the exact layer evaluated on the dequantised x and weights:
+    this pins where every scale enters."""
     rng = np.random.default_rng(18)
     T, D, E, k = 40, 32, 8, 3
     x = numerics.bf16_round(rng.standard_normal((T, D)).astype(np.float32))
@@ -446,7 +447,7 @@ def test_fp8_share_with_single_intermediate_channel_is_exact_layer_on_dequantise
     dq, ds = _fp8_weights(rng, E, D, 1)
     ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
     experts_q = [((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])) for e in range(E)]
-    got = oracle.layer_from_routing_fp8(x, ids, w, experts_q)
+    got = oracle.layer_from_routing_fp8(x, ids, w, experts_q, h_storage=None)
     xq, sx = oracle.quantize_rows_e4m3(x)
     x_deq = xq * sx.astype(np.float64)[:, None]
     deq = [(gq[e] * gs[e][:, None], uq[e] * us[e][:, None], dq[e] * ds[e][:, None]) for e in range(E)]
@@ -475,6 +476,34 @@ def test_fp8_layer_shared_expert_runs_unquantised_on_x_with_weight_one():
     shared_only = oracle.layer_from_routing(x, ids, np.zeros_like(w), deq, shared=sh)["y"]
     assert np.abs(shared_only).max() > 0.1
     np.testing.assert_allclose(got, routed + shared_only, rtol=0, atol=1e-12 * np.abs(got).max())
+
+
+def test_fp8_share_quantises_h_from_its_bf16_values():
+    """By default h is stored as bf16 before its per-row quantisation: the h that enters the
+    quantiser lies on the bf16 grid, within half a bf16 step of the float64 h (the step of its
+    binade, 2**(e-7) for 2**e <= |h| < 2**(e+1), plus the binary32 rounding taken first), and
+    the layer with h_storage=None (float64 h) differs from it; a dropped, truncating or
+    wrong-grid rounding fails one of these."""
+    rng = np.random.default_rng(31)
+    T, D, E, k, I = 48, 64, 6, 2, 32
+    x = numerics.bf16_round(rng.standard_normal((T, D)).astype(np.float32))
+    gq, gs = _fp8_weights(rng, E, I, D)
+    uq, us = _fp8_weights(rng, E, I, D)
+    dq, ds = _fp8_weights(rng, E, D, I)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    experts_q = [((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])) for e in range(E)]
+    got = oracle.layer_from_routing_fp8(x, ids, w, experts_q)
+    raw = oracle.layer_from_routing_fp8(x, ids, w, experts_q, h_storage=None)
+    h, h64 = got["h"], raw["h"]
+    assert h.shape == (T * k, I)
+    np.testing.assert_array_equal(numerics.bf16_round(h), h)
+    _, ex = np.frexp(h)                                  # |h| = m * 2**ex, m in [0.5, 1)
+    half_step = np.ldexp(1.0, ex - 9)                    # half of 2**((ex - 1) - 7)
+    assert np.all(np.abs(h - h64) <= half_step * (1 + 2.0 ** -15))
+    assert np.any(h != h64)
+    assert not np.array_equal(got["y"], raw["y"])
+    with pytest.raises(ValueError):
+        oracle.layer_from_routing_fp8(x, ids, w, experts_q, h_storage="e4m3")
 
 
 def test_fp8_share_close_to_exact_layer():
