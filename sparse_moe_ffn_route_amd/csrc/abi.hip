@@ -446,19 +446,14 @@ int moe_layer_forward(const moe_dims* dims, const moe_weights* w, const void* x,
   int32_t* perm = at<int32_t>(ws, L.perm_token);
   int32_t* inv = at<int32_t>(ws, L.inv_pos);
   const int bm = gemm_bm(expert_shape(d, true));
+  // with e4m3 experts the grouping launches also quantise x per token
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.E, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
                          at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), at<int32_t>(ws, L.bad), counts, offsets,
                          perm, inv, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b), at<int32_t>(ws, L.err),
-                         s));
-  const void* a_rows = x;
-  const float* a_scale = nullptr;
-  if (fp8) {
-    // tokens without a local slot (other devices' experts only) are not quantised
-    MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s, inv,
-                              d.top_k));
-    a_rows = at<void>(ws, L.xq);
-    a_scale = at<float>(ws, L.sx);
-  }
+                         s, fp8 ? x : nullptr, d.D, fp8 ? at<void>(ws, L.xq) : nullptr,
+                         fp8 ? at<float>(ws, L.sx) : nullptr));
+  const void* a_rows = fp8 ? at<void>(ws, L.xq) : x;
+  const float* a_scale = fp8 ? at<float>(ws, L.sx) : nullptr;
   MOE_TRY(mark(2));
 
   // 3. experts; with a shared expert its down projection also does step 4 (the unpermute-

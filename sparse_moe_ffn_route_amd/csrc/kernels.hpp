@@ -60,10 +60,16 @@ hipError_t launch_route(const float* parts, int n_parts, float* logits, const fl
 // pairs whose id lies outside [0, E) (skipped like any non-local pair).
 //   hist, base: [perm_units(T, k)][n_local] scratch; rank: [T * k] scratch;
 //   bad: [perm_units(T, k)] scratch.
+// xq_src (nullable): bf16 token rows [T][xq_cols], quantised per row to E4M3 into xq_dst
+// [T][xq_cols] and xq_scale [T] as launch_quant_rows does.  On the multi-workgroup path
+// every row is quantised by workgroups of the ranking launch, beside the ranking; on the
+// one-workgroup path rows without a local slot are skipped (left unwritten) by a launch
+// after the grouping.  The grouped GEMMs read only rows with a local slot.
 hipError_t launch_permute(const int32_t* packed, int T, int k, int E, int e_begin, int n_local, int32_t* hist,
                           int32_t* base, int32_t* rank, int32_t* bad, int32_t* counts, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0,
-                          int32_t* prefix1, int32_t* err_word, hipStream_t stream);
+                          int32_t* prefix1, int32_t* err_word, hipStream_t stream, const void* xq_src = nullptr,
+                          int xq_cols = 0, void* xq_dst = nullptr, float* xq_scale = nullptr);
 
 hipError_t launch_gather_rows(const void* src, const float* src_scale, const int32_t* perm_token,
                               const int32_t* n_rows_dev, int max_rows, int row_bytes, void* dst, float* dst_scale,

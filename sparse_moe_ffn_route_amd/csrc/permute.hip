@@ -45,18 +45,33 @@ __device__ __forceinline__ int local_expert_checked(const int32_t* packed, int i
   return (e >= 0 && e < n_local) ? e : -1;
 }
 
+// Per-row E4M3 quantisation of row r by one wave (defined with quant_rows_kernel).
+template <int IN>
+__device__ __forceinline__ void quant_row(const void* __restrict__ src, int r, int cols, int lane,
+                                          uint8_t* __restrict__ dst, float* __restrict__ scale);
+
 // Stage 1 of the multi-workgroup grouping: one wave per unit of kPermUnit consecutive
 // pairs.  The wave loads all its pairs first (one memory latency), then walks them 64
 // at a time: lanes holding the same expert find each other with one ballot per id bit,
 // rank themselves by lane order, and the lowest lane advances that expert's running
 // count in LDS.  Output: each local pair's rank inside its unit, hist[unit][e], and
 // bad[unit], the unit's pairs whose id lies outside [0, E).
+// Workgroups from rank_blocks on quantise the bf16 token rows qsrc [qrows][qcols] to
+// E4M3 (one wave per row): that needs nothing from the grouping, so it runs beside the
+// ranking instead of after the grouping.
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ packed, int n_pairs, int k,
                                                         int e_begin, int n_local, int E, int n_bits, int n_units,
                                                         int32_t* __restrict__ rank, int32_t* __restrict__ hist,
-                                                        int32_t* __restrict__ bad) {
+                                                        int32_t* __restrict__ bad, int rank_blocks,
+                                                        const void* __restrict__ qsrc, int qrows, int qcols,
+                                                        uint8_t* __restrict__ qdst, float* __restrict__ qscale) {
   __shared__ int32_t run[kWavesPerBlock][kMaxLocalExperts];
   const int w = threadIdx.x / kWave, lane = lane_id();
+  if (static_cast<int>(blockIdx.x) >= rank_blocks) {
+    const int r = (static_cast<int>(blockIdx.x) - rank_blocks) * kWavesPerBlock + w;
+    if (r < qrows) quant_row<EL_BF16>(qsrc, r, qcols, lane, qdst, qscale);
+    return;
+  }
   const int u = blockIdx.x * kWavesPerBlock + w;
   if (u >= n_units) return;  // whole wave leaves together; waves use disjoint LDS rows
   const int base_i = u * kPermUnit;
@@ -393,21 +408,9 @@ __device__ __forceinline__ void quant_row_in_regs(const void* __restrict__ src, 
   if (lane == 0) scale[r] = s;
 }
 
-// skip_inv: NULL, or inv_pos [rows][skip_k]: a row whose k slots are all non-local
-// (inv_pos < 0) is never read by the grouped GEMMs and is left unwritten.
 template <int IN>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int rows,
-                                                         const int32_t* __restrict__ n_rows_dev, int cols,
-                                                         uint8_t* __restrict__ dst, float* __restrict__ scale,
-                                                         const int32_t* __restrict__ skip_inv, int skip_k) {
-  const int r = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int n = n_rows_dev ? *n_rows_dev : rows;
-  if (r >= n) return;
-  if (skip_inv) {
-    const bool used = lane < skip_k && skip_inv[static_cast<size_t>(r) * skip_k + lane] >= 0;
-    if (__ballot(used) == 0) return;  // wave-uniform
-  }
+__device__ __forceinline__ void quant_row(const void* __restrict__ src, int r, int cols, int lane,
+                                          uint8_t* __restrict__ dst, float* __restrict__ scale) {
   if (cols <= kWave * 8 * 2) return quant_row_in_regs<IN, 2>(src, r, cols, lane, dst, scale);
   if (cols <= kWave * 8 * 4) return quant_row_in_regs<IN, 4>(src, r, cols, lane, dst, scale);
   if (cols <= kWave * 8 * 8) return quant_row_in_regs<IN, 8>(src, r, cols, lane, dst, scale);
@@ -462,6 +465,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   if (lane == 0) scale[r] = s;
 }
 
+// skip_inv: NULL, or inv_pos [rows][skip_k]: a row whose k slots are all non-local
+// (inv_pos < 0) is never read by the grouped GEMMs and is left unwritten.
+template <int IN>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int rows,
+                                                         const int32_t* __restrict__ n_rows_dev, int cols,
+                                                         uint8_t* __restrict__ dst, float* __restrict__ scale,
+                                                         const int32_t* __restrict__ skip_inv, int skip_k) {
+  const int r = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int n = n_rows_dev ? *n_rows_dev : rows;
+  if (r >= n) return;
+  if (skip_inv) {
+    const bool used = lane < skip_k && skip_inv[static_cast<size_t>(r) * skip_k + lane] >= 0;
+    if (__ballot(used) == 0) return;  // wave-uniform
+  }
+  quant_row<IN>(src, r, cols, lane, dst, scale);
+}
+
 // Tile schedule: prefix[g] = sum over groups g' < g of ceil(rows_g' / bm), for two
 // tile heights at once.  One workgroup of 1024 threads (n_groups <= 1024).
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int n_groups,
@@ -501,19 +522,24 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 hipError_t launch_permute(const int32_t* packed, int T, int k, int E, int e_begin, int n_local, int32_t* hist,
                           int32_t* base, int32_t* rank, int32_t* bad, int32_t* counts, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv_pos, int bm0, int bm1, int32_t* prefix0,
-                          int32_t* prefix1, int32_t* err_word, hipStream_t stream) {
+                          int32_t* prefix1, int32_t* err_word, hipStream_t stream, const void* xq_src, int xq_cols,
+                          void* xq_dst, float* xq_scale) {
   const int n_pairs = T * k;
   int n_bits = 1;
   while ((1 << n_bits) < n_local) ++n_bits;
   if (n_pairs <= kFusedWaves * kWave * 8) {
     hipLaunchKernelGGL(perm_fused_kernel<8>, dim3(1), dim3(1024), 0, stream, packed, n_pairs, k, e_begin, n_local,
                        n_bits, bm0, bm1, counts, offsets, perm_token, inv_pos, prefix0, prefix1, E, err_word);
-    return hipGetLastError();
+    if (!xq_src) return hipGetLastError();
+    // tokens without a local slot (other devices' experts only) are not quantised
+    return launch_quant_rows(EL_BF16, xq_src, T, nullptr, xq_cols, xq_dst, xq_scale, stream, inv_pos, k);
   }
   const int n_units = perm_units(T, k);
   const int blocks = (n_units + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(perm_rank_kernel, dim3(blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin, n_local,
-                     E, n_bits, n_units, rank, hist, bad);
+  const int q_blocks = xq_src ? (T + kWavesPerBlock - 1) / kWavesPerBlock : 0;
+  hipLaunchKernelGGL(perm_rank_kernel, dim3(blocks + q_blocks), dim3(256), 0, stream, packed, n_pairs, k, e_begin,
+                     n_local, E, n_bits, n_units, rank, hist, bad, blocks, xq_src, xq_src ? T : 0, xq_cols,
+                     static_cast<uint8_t*>(xq_dst), xq_scale);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, n_local, n_units, bm0, bm1, base,
                      counts, offsets, prefix0, prefix1, bad, err_word);
   hipLaunchKernelGGL(perm_place_kernel, dim3((n_pairs + 255) / 256), dim3(256), 0, stream, packed, n_pairs, k,
