@@ -60,8 +60,10 @@ int router_shape(const moe_dims& d) {
 }
 
 // K splits of the router projection (partial sums added in order by the route kernel):
-// enough workgroups to cover the chip, at most 512 tiles in the streaming shape and
-// at least 256 (with at most 4 partial products) in the tile shape.
+// enough workgroups to cover the chip, at most 256 tiles in the streaming shape (one per
+// CU: at 512 tokens and 512 experts four partial sums, where eight or two made the
+// routing stage slower) and at least 256 (with at most 4 partial products) in the tile
+// shape.
 int router_splits(const moe_dims& d) {
   const int shape = router_shape(d);
   const int row_bytes = d.D * act_size(d.act_dtype);
@@ -74,7 +76,7 @@ int router_splits(const moe_dims& d) {
   if (shape == kShapeTile256) {
     while (s < 4 && tiles * s < 256 && s * 2 <= blocks && blocks % (s * 2) == 0) s *= 2;
   } else {
-    while (s * 2 <= blocks && blocks % (s * 2) == 0 && tiles * s * 2 <= 512) s *= 2;
+    while (s * 2 <= blocks && blocks % (s * 2) == 0 && tiles * s * 2 <= 256) s *= 2;
   }
   return s;
 }
