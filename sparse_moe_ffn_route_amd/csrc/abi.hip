@@ -359,14 +359,16 @@ int moe_permute(const moe_dims* dims, const int32_t* packed, int32_t* counts, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.T == 0) return MOE_OK;
   const int bm = gemm_bm(expert_shape(d, true));
+  // e4m3: x is quantised per token by the grouping launches, as in the layer call
+  const bool quant = x && fp8;
   MOE_TRY(launch_permute(packed, d.T, d.top_k, d.E, d.expert_begin, d.n_local, at<int32_t>(ws, L.hist),
                          at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), at<int32_t>(ws, L.bad), counts, offsets,
                          perm_token, inv_pos, bm, bm, at<int32_t>(ws, L.tp_a), at<int32_t>(ws, L.tp_b),
-                         at<int32_t>(ws, L.err), s));
+                         at<int32_t>(ws, L.err), s, quant ? x : nullptr, d.D, quant ? at<void>(ws, L.xq) : nullptr,
+                         quant ? at<float>(ws, L.sx) : nullptr));
   if (x) {
     const int tk = d.T * d.top_k;
     if (fp8) {
-      MOE_TRY(launch_quant_rows(EL_BF16, x, d.T, nullptr, d.D, at<void>(ws, L.xq), at<float>(ws, L.sx), s));
       MOE_TRY(launch_gather_rows(at<void>(ws, L.xq), at<float>(ws, L.sx), perm_token, offsets + d.n_local, tk, d.D,
                                  x_perm, x_perm_scale, s));
     } else {

@@ -463,35 +463,37 @@ def test_layer_with_corrupt_given_blob_skips_and_counts_bad_ids():
     assert rel_err(g["y"], ref["y"]) <= tolerance(wl)
 
 
-def test_permute_gathers_rows_and_quantises_fp8():
-    T, k, E, D = 300, 4, 24, 256
+@pytest.mark.parametrize("T,k,E,begin,n_local", [(300, 4, 24, 0, 24), (2600, 4, 32, 8, 16)])
+def test_permute_gathers_rows_and_quantises_fp8(T, k, E, begin, n_local):
+    """Gathered rows through moe_permute.  The second case has 10,400 pairs (the multi-workgroup grouping, whose
+    ranking launch also quantises x) and a slice, so some tokens have no local slot."""
+    D = 256
     rng = np.random.default_rng(2)
     packed, ids = _packed_blob(rng, T, k, E, False)
     x = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
     x[7] = 0                                                 # an all-zero token: scale 1
-    # bf16 gather: permute then unpermute is the identity
-    d = moe.make_dims(T, D, E, k, 64)
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    c, o, p, iv = oracle.permute(ids, begin, n_local)
+    n_a = int(o[-1])
+    # bf16 gather: every local slot's row is its token's row
+    d = moe.make_dims(T, D, E, k, 64, expert_begin=begin, n_local=n_local)
+    counts = torch.empty(n_local, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(n_local + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     inv = torch.empty(T, k, dtype=torch.int32, device="cuda")
     xp = torch.empty(T * k, D, dtype=torch.bfloat16, device="cuda")
     moe.moe_permute(d, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, x.cuda(), xp, None,
                     ws=moe.workspace(d))
-    xp_h, inv_h = xp.cpu(), inv.cpu().numpy()
-    for t in range(T):
-        for j in range(k):
-            assert torch.equal(xp_h[inv_h[t, j]], x[t])
+    np.testing.assert_array_equal(inv.cpu().numpy(), iv)
+    np.testing.assert_array_equal(xp.cpu()[:n_a].view(torch.int16).numpy(),
+                                  x[torch.from_numpy(p.astype(np.int64))].view(torch.int16).numpy())
     # fp8 gather: per-token E4M3 codes and scales, bit-exact against the oracle's quantiser
-    d8 = moe.make_dims(T, D, E, k, 64, w="e4m3")
+    d8 = moe.make_dims(T, D, E, k, 64, expert_begin=begin, n_local=n_local, w="e4m3")
     xq = torch.empty(T * k, D, dtype=torch.uint8, device="cuda")
     xs = torch.empty(T * k, dtype=torch.float32, device="cuda")
     moe.moe_permute(d8, torch.from_numpy(packed).cuda(), counts, offsets, perm, inv, x.cuda(), xq, xs,
                     ws=moe.workspace(d8))
     q_ref, s_ref = oracle.quantize_rows_e4m3(to_np(x))
     codes_ref = oracle.e4m3_encode(q_ref)
-    c, o, p, iv = oracle.permute(ids, 0, E)
-    n_a = int(o[-1])
     np.testing.assert_array_equal(xq.cpu().numpy()[:n_a], codes_ref[p])
     np.testing.assert_array_equal(xs.cpu().numpy()[:n_a], s_ref[p])
 
