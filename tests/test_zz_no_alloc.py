@@ -3,7 +3,11 @@
 It launches the same kernels as moe_layer_forward, so y, the logits and the
 routing blob must equal those of moe_layer_forward with a caller workspace bit
 for bit, on two calls in a row (the second with a smaller batch, over what the
-first call left in the scratch), and the output also meets the oracle's bar.
+first call left in the scratch), and the output also meets the oracle's bar.  It is
+meant for callers that capture their launches in a graph: captured after one eager call
+(the static scratch's address is looked up on a device's first call), every replay, with
+eager layer calls on other inputs over the same scratch in between, reproduces the eager
+result bit for bit.
 """
 
 import numpy as np
@@ -117,3 +121,60 @@ def test_noalloc_rejects_dims_beyond_the_static_scratch():
     st = lib.moe_layer_forward_noalloc(moe.ctypes.byref(d), moe.ctypes.byref(w), p, None, None, p, None, None, None,
                                        None, None)
     assert st == moe.ERR_SCRATCH_LIMIT
+
+
+GRAPH_WL = W("graph_small", T=300, D=512, E=40, top_k=4, I=192, I_shared=128, act="bf16", w="bf16", out="bf16")
+
+
+def _graph_weights(dev):
+    return moe.make_weights(dev.w_router, dev.w_gate, dev.w_up, dev.w_down, None, None, None,
+                            dev.ws_gate, dev.ws_up, dev.ws_down)
+
+
+def _graph_outputs():
+    wl = GRAPH_WL
+    return dict(y=torch.full((wl.T, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                logits=torch.full((wl.T, wl.E), float("nan"), dtype=torch.float32, device="cuda"),
+                blob=torch.full((wl.T, 2, wl.top_k), -7, dtype=torch.int32, device="cuda"),
+                bad=torch.full((1,), -1, dtype=torch.int32, device="cuda"))
+
+
+def _graph_call(d, w, x, o):
+    moe.moe_layer_forward_noalloc(d, w, x, None, None, o["y"], o["logits"], o["blob"], o["bad"])
+
+
+def _graph_same(a, b):
+    assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
+    assert torch.equal(a["logits"], b["logits"])
+    assert torch.equal(a["blob"], b["blob"])
+    assert torch.equal(a["bad"], b["bad"])
+
+
+def test_noalloc_layer_replays_in_a_graph():
+    wl = GRAPH_WL
+    print(f"[graph] {wl.name}: eager call, capture, three replays", flush=True)
+    d = dims_of(wl)
+    dev = synth.make_inputs(wl, 4, "cpu").to("cuda")
+    other = synth.make_inputs(wl, 5, "cpu").to("cuda")
+    w, w_other = _graph_weights(dev), _graph_weights(other)
+    ref = _graph_outputs()
+    _graph_call(d, w, dev.x, ref)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref.items()}
+    out = _graph_outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _graph_call(d, w, dev.x, out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        eager = _graph_outputs()
+        _graph_call(d, w_other, other.x, eager)      # another layer call over the same static scratch
+        torch.cuda.synchronize()
+        assert not torch.equal(eager["y"].view(torch.int16), ref["y"].view(torch.int16))
+        for v in out.values():
+            v.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {i} done", flush=True)
+        _graph_same(out, ref)
